@@ -1,0 +1,268 @@
+"""Oracle radix tree over token prefixes: plain, slow, obviously correct.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product imports this module; only
+tests/, the smoke check and the bench's CPU-baseline leg call it.
+
+What it follows (pages as given, sections named):
+
+* "SGLang: the tree, and the language nobody remembers" (ai.thesatyajit.com),
+  section "A tree, not a map": a radix tree over token prefixes whose nodes
+  carry a key (token run), a value (one KV slot per token), children keyed on
+  the first token, lock_ref, last-access time and priority; a node splits at
+  the divergence point; inc/dec of lock_ref moves len(key) between the
+  evictable and protected totals on the 0<->1 edge; eviction pops evictable
+  leaves off a heap and pushes a parent that became childless and unlocked.
+* "SGLang" (bibekananda.in), sections "One tree for everybody" and "Eviction
+  on a tree": walk from the root while tokens match, everything matched is
+  reuse; eviction runs from the leaves inward.
+* "How does SGLang work" (modernaiengineering.com), sections "What happens
+  when a request arrives" (match, lock, prefill the rest, insert, unlock)
+  and "Worked example, step by step" (least recently used unlocked leaf goes
+  first, a node is evicted whole, nothing evictable means the request waits).
+
+Readings where the pages are silent (each listed in the design notes):
+page_size 1; a logical clock that ticks once per match/insert call and
+stamps every node the call visits; heap key (priority, last_access, node id)
+with priority 0; splits in both match and insert, the new upper node taking
+a fresh id and the lower node's lock_ref and last_access; lowest-free-first
+slot allocation; insert over present tokens keeps the tree's slots and frees
+the caller's differing ones; node ids are never reused, root = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+class NoSpace(Exception):
+    """Allocation could not be satisfied even after evicting every evictable node."""
+
+
+class Stale(Exception):
+    """A node id that no longer names a node in the tree."""
+
+
+class Node:
+    __slots__ = ("id", "key", "value", "children", "parent", "lock_ref", "last_access", "priority")
+
+    def __init__(self, nid, key, value, parent):
+        self.id = nid
+        self.key = np.asarray(key, dtype=np.int32)
+        self.value = np.asarray(value, dtype=np.int32)
+        self.children = {}          # first token -> Node
+        self.parent = parent
+        self.lock_ref = 0
+        self.last_access = 0
+        self.priority = 0
+
+
+def common_prefix_len(a: np.ndarray, b: np.ndarray) -> int:
+    """Number of leading positions where a and b agree."""
+    n = min(len(a), len(b))
+    if n == 0:
+        return 0
+    diff = np.flatnonzero(a[:n] != b[:n])
+    return int(diff[0]) if len(diff) else n
+
+
+class RadixTree:
+    def __init__(self, pool_slots: int):
+        self.pool_slots = int(pool_slots)
+        self.root = Node(0, [], [], None)
+        self.nodes = {0: self.root}
+        self.next_id = 1
+        self.clock = 0
+        self.free = np.ones(self.pool_slots, dtype=bool)   # True = slot is free
+        self.evictable = 0
+        self.protected = 0
+        self.evicted_total = 0
+
+    # ---------------------------------------------------------------- helpers
+    def _node(self, nid) -> Node:
+        n = self.nodes.get(int(nid))
+        if n is None:
+            raise Stale(nid)
+        return n
+
+    def _new_id(self) -> int:
+        i = self.next_id
+        self.next_id += 1
+        return i
+
+    def _split(self, child: Node, k: int) -> Node:
+        """Cut child's edge after k tokens; the new upper node is returned."""
+        upper = Node(self._new_id(), child.key[:k], child.value[:k], child.parent)
+        upper.lock_ref = child.lock_ref
+        upper.last_access = child.last_access
+        upper.priority = child.priority
+        upper.parent.children[int(child.key[0])] = upper
+        child.key = child.key[k:]
+        child.value = child.value[k:]
+        child.parent = upper
+        upper.children[int(child.key[0])] = child
+        self.nodes[upper.id] = upper
+        return upper
+
+    # ---------------------------------------------------------------- match
+    def match_prefix(self, tokens):
+        """Longest cached prefix of `tokens`.  Returns (slots, node id)."""
+        tokens = np.asarray(tokens, dtype=np.int32)
+        self.clock += 1
+        node, pos, got = self.root, 0, []
+        while pos < len(tokens) and int(tokens[pos]) in node.children:
+            child = node.children[int(tokens[pos])]
+            child.last_access = self.clock
+            k = common_prefix_len(child.key, tokens[pos:])
+            if k < len(child.key):
+                child = self._split(child, k)
+            got.append(child.value)
+            pos += k
+            node = child
+        slots = np.concatenate(got) if got else np.zeros(0, np.int32)
+        return slots, node.id
+
+    # ---------------------------------------------------------------- insert
+    def insert(self, tokens, slots):
+        """Insert tokens with their slots.  Returns (prefix_len, node id, slots).
+
+        prefix_len tokens were already present; for them the tree's slots are
+        kept, any differing caller slot is freed, and the returned slots array
+        carries the tree's ids.  The remaining slots are adopted by a new leaf.
+        """
+        tokens = np.asarray(tokens, dtype=np.int32)
+        slots = np.array(slots, dtype=np.int32, copy=True)
+        assert len(tokens) == len(slots)
+        self.clock += 1
+        node, pos = self.root, 0
+        while pos < len(tokens) and int(tokens[pos]) in node.children:
+            child = node.children[int(tokens[pos])]
+            child.last_access = self.clock
+            k = common_prefix_len(child.key, tokens[pos:])
+            if k < len(child.key):
+                child = self._split(child, k)
+            seg = slots[pos:pos + k]
+            differ = seg != child.value
+            if differ.any():
+                self._free(seg[differ])
+                seg[differ] = child.value[differ]
+            pos += k
+            node = child
+        prefix = pos
+        if pos < len(tokens):
+            leaf = Node(self._new_id(), tokens[pos:], slots[pos:], node)
+            leaf.last_access = self.clock
+            node.children[int(tokens[pos])] = leaf
+            self.nodes[leaf.id] = leaf
+            self.evictable += len(leaf.key)
+            node = leaf
+        return prefix, node.id, slots
+
+    # ---------------------------------------------------------------- locks
+    def inc_lock_ref(self, nid):
+        node = self._node(nid)
+        while node is not self.root:
+            if node.lock_ref == 0:
+                self.evictable -= len(node.key)
+                self.protected += len(node.key)
+            node.lock_ref += 1
+            node = node.parent
+
+    def dec_lock_ref(self, nid):
+        node = self._node(nid)
+        if node is not self.root and node.lock_ref <= 0:
+            raise ValueError("dec_lock_ref below zero")
+        while node is not self.root:
+            if node.lock_ref == 1:
+                self.evictable += len(node.key)
+                self.protected -= len(node.key)
+            node.lock_ref -= 1
+            node = node.parent
+
+    # ---------------------------------------------------------------- slots
+    def _free(self, slots):
+        s = np.asarray(slots, dtype=np.int64)
+        assert not self.free[s].any(), "double free"
+        self.free[s] = True
+
+    def free_slots(self, slots):
+        self._free(slots)
+
+    def num_free(self) -> int:
+        return int(self.free.sum())
+
+    def alloc(self, n: int) -> np.ndarray:
+        """n free slots, lowest ids first; evicts to fit; NoSpace if it cannot."""
+        n = int(n)
+        have = self.num_free()
+        if have < n:
+            self.evict(n - have)
+            if self.num_free() < n:
+                raise NoSpace(n)
+        got = np.flatnonzero(self.free)[:n]
+        self.free[got] = False
+        return got.astype(np.int32)
+
+    # ---------------------------------------------------------------- evict
+    def _evictable_leaves(self):
+        return [nd for nd in self.nodes.values()
+                if nd is not self.root and not nd.children and nd.lock_ref == 0]
+
+    def evict(self, num_tokens: int) -> int:
+        """Evict whole unlocked leaves, least key first, until num_tokens are freed."""
+        import heapq
+        heap = [(nd.priority, nd.last_access, nd.id) for nd in self._evictable_leaves()]
+        heapq.heapify(heap)
+        freed = 0
+        while freed < num_tokens and heap:
+            _p, _t, nid = heapq.heappop(heap)
+            x = self.nodes[nid]
+            self._free(x.value)
+            freed += len(x.value)
+            self.evictable -= len(x.key)
+            parent = x.parent
+            del parent.children[int(x.key[0])]
+            del self.nodes[nid]
+            if parent is not self.root and not parent.children and parent.lock_ref == 0:
+                heapq.heappush(heap, (parent.priority, parent.last_access, parent.id))
+        self.evicted_total += freed
+        return freed
+
+    # ---------------------------------------------------------------- views
+    def path(self, nid):
+        """Nodes from the root's child down to nid."""
+        out, node = [], self._node(nid)
+        while node is not self.root:
+            out.append(node)
+            node = node.parent
+        return out[::-1]
+
+    def tree_tokens(self) -> int:
+        return sum(len(nd.key) for nd in self.nodes.values())
+
+    def stats(self) -> dict:
+        return {
+            "nodes": len(self.nodes) - 1,
+            "tree_tokens": self.tree_tokens(),
+            "evictable": self.evictable,
+            "protected": self.protected,
+            "free": self.num_free(),
+            "evicted_total": self.evicted_total,
+            "clock": self.clock,
+        }
+
+    def dump(self) -> str:
+        """Canonical text: depth-first, children in ascending first-token order.
+
+        One line per node: depth id lock_ref last_access len | key tokens | slots
+        """
+        lines = []
+
+        def walk(nd, depth):
+            for ft in sorted(nd.children):
+                c = nd.children[ft]
+                lines.append("%d %d %d %d %d | %s | %s" % (
+                    depth, c.id, c.lock_ref, c.last_access, len(c.key),
+                    " ".join(map(str, c.key.tolist())), " ".join(map(str, c.value.tolist()))))
+                walk(c, depth + 1)
+
+        walk(self.root, 0)
+        return "\n".join(lines) + ("\n" if lines else "")
