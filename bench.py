@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Benchmark of RadixAttention's hot path on one MI355X.
+
+One step = one pass of the device path over a resident batch: store the new
+tokens' K/V into their pool slots, extend attention for the extend requests,
+prefix-aware decode attention (plan-driven, fused LSE merge) for the decode
+requests.  The host tree admission, table build and plan build that produce
+the batch are timed separately and reported (`host_ms`).
+
+Default workload: the large mixed batch (128 x 512-token extends + 128 decodes,
+contexts 1k-32k, GQA 64/8, d128, bf16, 4M-slot pool).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+
+# ---------------------------------------------------------------------------- setup
+class State:
+    pass
+
+
+def _chunks(n, size):
+    for i in range(0, n, size):
+        yield i, min(n, i + size)
+
+
+def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
+    """Admit a workload through librs and make its batch resident on the GPU."""
+    import torch
+    import radix_tree_prefix_amd as rs
+
+    t_host = time.perf_counter()
+    wl = synth.make(cfg, **wl_kw)
+    vals = synth.Values(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    S, Hq, Hkv, D = wl.pool_slots, wl.Hq, wl.Hkv, wl.D
+    st = State()
+    st.wl, st.vals, st.dt = wl, vals, dt
+    st.tree = tree = rs.Tree(S)
+
+    # history: admit and release every sequence; record every fresh run of slots
+    runs = []
+    t0 = time.perf_counter()
+    for s in wl.history:
+        row, node, m = tree.admit(s, len(s), 0)
+        if len(s) > m:
+            runs.append((s, m, len(s), row[m:].copy()))
+        tree.dec_lock_ref(node)
+    st.history_s = time.perf_counter() - t0
+
+    # batch: admit every request in order, its slots straight into its table row
+    ld = max(r.seq_len for r in wl.requests)
+    table = np.full((wl.B, ld), -1, np.int32)
+    nodes = np.zeros(wl.B, np.int64)
+    matched = np.zeros(wl.B, np.int64)
+    t0 = time.perf_counter()
+    for r in wl.requests:
+        row, node, m = tree.admit(r.tokens, r.cached, r.new, out_row=table[r.row, :r.seq_len])
+        nodes[r.row], matched[r.row] = node, m
+        if r.cached > m:
+            runs.append((r.tokens, m, r.cached, row[m:r.cached]))
+    st.admit_s = time.perf_counter() - t0
+    st.table, st.nodes, st.matched, st.ld = table, nodes, matched, ld
+
+    # K/V of every written slot (last writer wins when an evicted slot was reused)
+    sl, ik, iv = [], [], []
+    for toks, lo, hi, slots in runs:
+        a, b = vals.kv_index(toks[:hi])
+        sl.append(slots); ik.append(a[lo:hi]); iv.append(b[lo:hi])
+    sl = np.concatenate(sl) if sl else np.zeros(0, np.int32)
+    ik = np.concatenate(ik) if ik else np.zeros(0, np.int64)
+    iv = np.concatenate(iv) if iv else np.zeros(0, np.int64)
+    _, first = np.unique(sl[::-1], return_index=True)
+    keep = len(sl) - 1 - first
+    sl, ik, iv = sl[keep], ik[keep], iv[keep]
+
+    st.k_pool = torch.zeros((S, Hkv, D), dtype=dt, device=device)
+    st.v_pool = torch.zeros((S, Hkv, D), dtype=dt, device=device)
+    ktab = torch.from_numpy(vals.k_table).to(device=device, dtype=dt)
+    vtab = torch.from_numpy(vals.v_table).to(device=device, dtype=dt)
+    qtab = torch.from_numpy(vals.q_table).to(device=device, dtype=dt)
+    for a, b in _chunks(len(sl), 1 << 18):
+        s_dev = torch.from_numpy(sl[a:b]).to(device)
+        kn = ktab.index_select(0, torch.from_numpy(ik[a:b]).to(device)).view(-1, Hkv, D)
+        vn = vtab.index_select(0, torch.from_numpy(iv[a:b]).to(device)).view(-1, Hkv, D)
+        rs.store_kv(st.k_pool, st.v_pool, kn, vn, s_dev)
+
+    # the step's inputs: new tokens' K/V and slots, queries, lengths, tables
+    ext = sorted(wl.extend_requests(), key=lambda r: r.row)
+    dec = sorted(wl.decode_requests(), key=lambda r: r.row)
+    if ext and dec:
+        assert max(r.row for r in ext) < min(r.row for r in dec), "extend rows must precede decode rows"
+    st.ext, st.dec = ext, dec
+    new_slots, new_ik, new_iv, q_ext_idx, q_dec_idx = [], [], [], [], []
+    for r in wl.requests:
+        a, b = vals.kv_index(r.tokens[:r.seq_len])
+        new_slots.append(table[r.row, r.cached:r.seq_len]); new_ik.append(a[r.cached:]); new_iv.append(b[r.cached:])
+    for r in ext:
+        q_ext_idx.append(vals.q_index(r.tokens[:r.seq_len])[r.cached:])
+    for r in dec:
+        q_dec_idx.append(vals.q_index(r.tokens[:r.seq_len])[r.seq_len - 1:])
+    new_slots = np.concatenate(new_slots)
+    st.n_new = len(new_slots)
+    st.new_slots = torch.from_numpy(new_slots).to(device)
+    st.k_new = ktab.index_select(0, torch.from_numpy(np.concatenate(new_ik)).to(device)).view(-1, Hkv, D)
+    st.v_new = vtab.index_select(0, torch.from_numpy(np.concatenate(new_iv)).to(device)).view(-1, Hkv, D)
+    st.table_dev = torch.from_numpy(table).to(device)
+    n_ext = len(ext)
+    if ext:
+        st.q_ext = qtab.index_select(0, torch.from_numpy(np.concatenate(q_ext_idx)).to(device)).view(-1, Hq, D)
+        st.out_ext = torch.empty_like(st.q_ext)
+        lens = np.array([r.new for r in ext], np.int32)
+        st.ext_tokens = int(lens.sum())
+        st.max_ext = int(lens.max())
+        st.qo_indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(device)
+        st.prefix_lens = torch.from_numpy(np.array([r.cached for r in ext], np.int32)).to(device)
+        st.extend_lens = torch.from_numpy(lens).to(device)
+        st.table_ext = st.table_dev[:n_ext]
+    if dec:
+        st.q_dec = qtab.index_select(0, torch.from_numpy(np.concatenate(q_dec_idx)).to(device)).view(-1, Hq, D)
+        st.out_dec = torch.empty_like(st.q_dec)
+        st.lse_dec = torch.empty((len(dec), Hq), dtype=torch.float32, device=device)
+        sl_ = np.array([r.seq_len for r in dec], np.int32)
+        st.dec_seq_lens = torch.from_numpy(sl_).to(device)
+        st.max_seq = int(sl_.max())
+        st.table_dec = st.table_dev[n_ext:]
+        st.plan = st.plan_dev = None
+        t0 = time.perf_counter()
+        if build_plan:
+            st.plan = rs.Plan(tree, nodes[n_ext:], np.array([r.cached for r in dec], np.int32), sl_, Hq, Hkv, D)
+            st.plan_dev = rs.upload_plan(st.plan, device)
+        st.plan_s = time.perf_counter() - t0
+        st.ws = rs.DecodeWorkspace(st.plan, len(dec), st.max_seq, Hq, Hkv, D, device)
+        st.ws_flat = rs.DecodeWorkspace(None, len(dec), st.max_seq, Hq, Hkv, D, device)
+    torch.cuda.synchronize()
+    st.host_s = time.perf_counter() - t_host
+    return st
+
+
+def run_store(st):
+    import radix_tree_prefix_amd as rs
+    rs.store_kv(st.k_pool, st.v_pool, st.k_new, st.v_new, st.new_slots)
+
+
+def run_extend(st):
+    import radix_tree_prefix_amd as rs
+    if st.ext:
+        rs.extend_attention(st.q_ext, st.k_pool, st.v_pool, st.table_ext, st.qo_indptr, st.prefix_lens,
+                            st.extend_lens, st.max_ext, st.wl.sm_scale, out=st.out_ext)
+
+
+def run_decode(st, flat=False):
+    import radix_tree_prefix_amd as rs
+    if st.dec:
+        if flat or st.plan is None:
+            rs.decode_attention(st.q_dec, st.k_pool, st.v_pool, st.table_dec, st.dec_seq_lens, st.max_seq,
+                                st.wl.sm_scale, st.ws_flat, out=st.out_dec, lse=st.lse_dec)
+        else:
+            rs.decode_attention(st.q_dec, st.k_pool, st.v_pool, st.table_dec, st.dec_seq_lens, st.max_seq,
+                                st.wl.sm_scale, st.ws, plan=st.plan, plan_dev=st.plan_dev, out=st.out_dec,
+                                lse=st.lse_dec)
+
+
+def step(st):
+    run_store(st)
+    run_extend(st)
+    run_decode(st)
+
+
+# ---------------------------------------------------------------------------- work counts
+def extend_flops(st):
+    """Exact causal flops: 4*D per (query head, visible key) pair."""
+    wl = st.wl
+    tot = 0
+    for r in st.ext:
+        P, E = r.cached, r.new
+        pairs = E * P + E * (E + 1) // 2
+        tot += pairs
+    return 4 * wl.D * wl.Hq * tot
+
+
+def decode_unique_bytes(st):
+    """Distinct KV positions the decode batch reads x bytes per position (K and V, all KV heads)."""
+    esz = 2 if st.wl.dtype == "bf16" else 4
+    slots = set()
+    for r in st.dec:
+        slots.update(st.table[r.row, :r.seq_len].tolist())
+    return len(slots) * 2 * st.wl.Hkv * st.wl.D * esz
+
+
+def decode_flat_bytes(st):
+    esz = 2 if st.wl.dtype == "bf16" else 4
+    return sum(r.seq_len for r in st.dec) * 2 * st.wl.Hkv * st.wl.D * esz
+
+
+# ---------------------------------------------------------------------------- timing
+def time_fn(fn, iters, warmup, flush=None):
+    """Median and mean device time (ms) of fn over iters launches, events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ts = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts)), float(np.mean(ts))
+
+
+def make_flush(device="cuda", nbytes=1 << 30):
+    """Overwrites a 1 GiB buffer so L2 and the 256 MB MALL hold none of the next op's inputs."""
+    import torch
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+
+    def flush():
+        buf.fill_(1)
+    return flush
+
+
+def cpu_baseline(st, budget_s=20.0):
+    """The oracle (fp64 numpy, per-request materialised KV) on a bounded sample of the batch."""
+    import oracle
+    wl, vals = st.wl, st.vals
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    toks = 0
+    sampled_ext = sampled_dec = 0
+    order = []
+    for i in range(max(len(st.ext), len(st.dec))):
+        if i < len(st.dec):
+            order.append(st.dec[i])
+        if i < len(st.ext):
+            order.append(st.ext[i])
+    for r in order:
+        if time.perf_counter() - t0 > budget_s:
+            break
+        k, v = vals.kv_rows(r.tokens, 0, r.seq_len)
+        q = vals.q_rows(r.tokens, r.cached if r.kind == "extend" else r.seq_len - 1, r.seq_len)
+        pos = np.arange(r.seq_len - len(q), r.seq_len)
+        oracle.attend(q, k, v, pos, wl.sm_scale)
+        toks += len(q)
+        if r.kind == "extend":
+            sampled_ext += 1
+        else:
+            sampled_dec += 1
+    dt = time.perf_counter() - t0
+    return {"value": toks / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sampled_ext} extend + {sampled_dec} decode requests of the batch "
+                      f"({toks} query tokens, {dt:.1f} s, KV regenerated per request, fp64 numpy)"}
+
+
+# ---------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel runs of the other configs")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path has no cross-GPU step); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "no GPU visible"
+    print(f"[bench] setup config {args.config}", file=sys.stderr, flush=True)
+    st = setup(args.config)
+    print(f"[bench] setup done in {st.host_s:.1f}s (history {st.history_s:.2f}s, admit {st.admit_s:.3f}s)",
+          file=sys.stderr, flush=True)
+
+    # the timed region: exactly K steps
+    for _ in range(args.warmup):
+        step(st)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        run_store(st)
+        e[1].record()
+        run_extend(st)
+        e[2].record()
+        run_decode(st)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ext_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    store_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tokens = (st.ext_tokens if st.ext else 0) + len(st.dec)
+    value = tokens / (ms_step / 1e3)
+
+    flops = extend_flops(st) if st.ext else 0
+    ub = decode_unique_bytes(st) if st.dec else 0
+    ext_tf = flops / (ext_ms / 1e3) / 1e12 if st.ext else 0.0
+    dec_gbs = ub / (dec_ms / 1e3) / 1e9 if st.dec else 0.0
+    if st.ext:
+        roof = {"bound": "mfma", "kernel": "extend_bf16_kernel<128>", "achieved": round(ext_tf, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ext_tf / BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "algorithmic_per_launch": flops, "avg_launch_ms": round(ext_ms, 4)}
+    else:
+        roof = {"bound": "hbm", "kernel": "decode_bf16_kernel<128>", "achieved": round(dec_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_per_launch": ub, "avg_launch_ms": round(dec_ms, 4)}
+    out = {
+        "metric": "decode+extend attention tokens/s and achieved HBM GB/s (% peak), 1 MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": st.wl.dtype, "data": "synthetic",
+        "config": {"workload": st.wl.name, "batch": st.wl.B, "extend_tokens": st.ext_tokens if st.ext else 0,
+                   "decode_requests": len(st.dec), "pool_slots": st.wl.pool_slots},
+        "roofline": roof,
+        "parts_ms": {"store_kv": round(store_ms, 4), "extend": round(ext_ms, 4), "decode": round(dec_ms, 4)},
+        "host_ms": {"history_admission": round(st.history_s * 1e3, 2), "batch_admission": round(st.admit_s * 1e3, 3),
+                    "decode_plan": round(getattr(st, "plan_s", 0.0) * 1e3, 3)},
+    }
+    if st.dec:
+        out["decode_hbm"] = {"achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "unique_kv_bytes": ub,
+                             "flat_kv_bytes": decode_flat_bytes(st)}
+    if not args.no_extra:
+        out["other_configs"] = extra_configs()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(st, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def extra_configs():
+    """Per-kernel numbers of the smaller workloads (cache-flushed medians)."""
+    import torch
+    res = {}
+    flush = make_flush()
+    for cfg in (2, 4, 3):
+        print(f"[bench] extra config {cfg}", file=sys.stderr, flush=True)
+        st = setup(cfg)
+        d = {"workload": st.wl.name}
+        if st.dec:
+            med, _ = time_fn(lambda: run_decode(st), 30, 5, flush)
+            medf, _ = time_fn(lambda: run_decode(st, flat=True), 30, 5, flush)
+            ub = decode_unique_bytes(st)
+            d.update({"decode_plan_us": round(med * 1e3, 2), "decode_flat_us": round(medf * 1e3, 2),
+                      "unique_kv_bytes": ub, "hbm_gbs_unique": round(ub / (med / 1e3) / 1e9, 1),
+                      "hbm_frac": round(ub / (med / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "tokens_per_s": round(len(st.dec) / (med / 1e3), 1)})
+        if st.ext:
+            med, _ = time_fn(lambda: run_extend(st), 20, 3, flush)
+            f = extend_flops(st)
+            d.update({"extend_us": round(med * 1e3, 2), "flops": f, "tflops": round(f / (med / 1e3) / 1e12, 2),
+                      "mfma_frac": round(f / (med / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "tokens_per_s": round(st.ext_tokens / (med / 1e3), 1)})
+        res[str(cfg)] = d
+        del st
+        torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

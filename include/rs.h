@@ -1,0 +1,251 @@
+/*
+ * rs.h -- C ABI of librs: RadixAttention's data-parallel hot path on one MI355X.
+ *
+ * A host radix tree over token prefixes indexes one token-granular KV pool, so
+ * requests that share a prefix point at the same pool slots and the shared KV
+ * is computed once.  Index tables built from the tree drive hand-written HIP
+ * kernels for gfx950: extend attention (prefill of only the unmatched suffix)
+ * and prefix-aware decode attention.
+ *
+ * Sources (pages, with section):
+ *  [T]  "SGLang: the tree, and the language nobody remembers" (ai.thesatyajit.com),
+ *       "A tree, not a map": node fields, split at divergence, lock_ref accounting,
+ *       heap eviction with cascade, page-1 child keys, galloping match.
+ *  [B]  "SGLang" (bibekananda.in), "One tree for everybody", "Eviction on a tree".
+ *  [L]  "How does SGLang work" (modernaiengineering.com): "A quick recap ..."
+ *       (prefill/decode, KV depends only on the prefix), "What happens when a
+ *       request arrives" (match, lock, prefill the rest, insert, unlock),
+ *       "Worked example, step by step" (LRU among unlocked leaves, whole nodes,
+ *       wait when nothing is evictable).
+ *  [P]  "SGLang" (llmdeepdive.com, lesson 8.5), "Conceito": the pool of blocks as
+ *       a radix tree keyed by token ids; allocate only for the divergent suffix.
+ *
+ * Conventions for every call:
+ *  - Return value: RS_OK (0) or a negative RS_E_* code; calls returning a count
+ *    return it (>= 0) or a negative code.  rs_last_error() gives a message for
+ *    the calling thread's last failure.  Nothing throws across the ABI.
+ *  - Ownership: the library owns only rs_tree and rs_plan objects.  Every array
+ *    argument is owned by the caller and only read or written during the call,
+ *    except device arrays of asynchronous calls (see below).
+ *  - Host vs device: "host" arrays are ordinary CPU memory; "device" arrays are
+ *    device memory of the current HIP device.  `stream` is a hipStream_t (NULL =
+ *    the default stream).  Device calls enqueue work and return without waiting;
+ *    their device arrays must stay valid until the stream reaches that point.
+ *  - A tree or plan handle must not be used by two threads at once.
+ *  - Node ids are int64, never reused; the root is 0.  A node id whose node has
+ *    been evicted is stale (RS_E_STALE).
+ *  - Layouts: K and V pools are [pool_slots][Hkv][D] row-major (one slot's row is
+ *    Hkv*D contiguous elements).  Index tables are int32 [B][ld] row-major; entry
+ *    (b, j) is the pool slot of position j of request b.  Query head h reads KV
+ *    head h / (Hq/Hkv).
+ *  - dtype: RS_DTYPE_F32 or RS_DTYPE_BF16 (bfloat16 bits).  Supported head dims:
+ *    64 and 128; Hq % Hkv == 0; Hq/Hkv <= 128.
+ */
+#ifndef RS_H_
+#define RS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RS_OK = 0,
+  RS_E_INVAL = -1,        /* bad argument or call sequence */
+  RS_E_NOSPACE = -2,      /* slots cannot be found even after eviction: the request waits [L] */
+  RS_E_STALE = -3,        /* node id no longer in the tree */
+  RS_E_HIP = -4,          /* a HIP runtime call failed */
+  RS_E_UNSUPPORTED = -5   /* shape or dtype outside what the kernels implement */
+};
+
+enum { RS_DTYPE_F32 = 0, RS_DTYPE_BF16 = 1 };
+
+typedef struct rs_tree rs_tree;
+typedef struct rs_plan rs_plan;
+
+typedef struct rs_stats_t {
+  int64_t pool_slots;
+  int64_t nodes;          /* excluding the root */
+  int64_t tree_tokens;    /* sum of key lengths */
+  int64_t evictable;      /* tokens in nodes with lock_ref == 0 [T] */
+  int64_t protected_;     /* tokens in nodes with lock_ref > 0 [T] */
+  int64_t free_slots;
+  int64_t evicted_total;  /* tokens freed by eviction since creation */
+  int64_t clock;          /* logical clock: +1 per match or insert call */
+  int64_t matched_total;  /* tokens returned by rs_match_prefix since creation */
+  int64_t match_calls;
+  int64_t insert_calls;
+  int64_t reserved[5];
+} rs_stats_t;
+
+typedef struct rs_plan_info_t {
+  int32_t B, Hq, Hkv, D;
+  int32_t n_items;          /* work items per KV head (grid x of the decode launch) */
+  int32_t n_segments;       /* segments: shared ones first, then one unique tail per request */
+  int32_t n_shared;         /* segments read by >= 2 requests */
+  int32_t chunk;            /* keys per work item (last chunk of a segment may be shorter) */
+  int64_t n_partials;       /* partial (o, lse) records per KV head per query head of a group */
+  int64_t unique_kv_tokens; /* distinct positions read: sum of segment lengths */
+  int64_t flat_kv_tokens;   /* sum of seq_lens: what a per-request read would touch */
+  int64_t bytes;            /* size of the device image rs_decode_plan_upload writes */
+  int64_t reserved[4];
+} rs_plan_info_t;
+
+/* Message for the calling thread's last failure ("" if none). */
+const char* rs_last_error(void);
+const char* rs_version(void);
+
+/* ------------------------------------------------------------------ tree [T][B][L] */
+
+/* New empty tree over pool slots 0..pool_slots-1, all free.  page_size must be 1
+ * (token-granular; children keyed on their first token [T]).  NULL on failure. */
+rs_tree* rs_tree_create(int64_t pool_slots, int32_t page_size);
+void rs_tree_destroy(rs_tree* t);
+
+/* Longest cached prefix of tokens[0..n) [B "One tree for everybody"].  Walks from the
+ * root comparing edges with a galloping search [T]; if the match ends inside an edge the
+ * node is split there (the upper part gets a fresh id and the lower part's lock_ref and
+ * last_access; the lower part keeps its id) [T].  Every node visited gets the current
+ * clock tick.  Writes the matched slots to out_slots (host, capacity >= n), their count
+ * to *out_len and the node the match ends at to *out_node (0 = root, empty match). */
+int rs_match_prefix(rs_tree* t, const int32_t* tokens, int64_t n,
+                    int32_t* out_slots, int64_t* out_len, int64_t* out_node);
+
+/* lock_ref +1 / -1 on node and every ancestor up to the root.  On the 0->1 edge a
+ * node's key length moves from evictable to protected, and back on 1->0 [T].
+ * rs_dec_lock_ref on a node whose lock_ref is 0 is RS_E_INVAL (nothing changes). */
+int rs_inc_lock_ref(rs_tree* t, int64_t node);
+int rs_dec_lock_ref(rs_tree* t, int64_t node);
+
+/* n free slots, lowest ids first, ascending, into out_slots (host).  When fewer than
+ * n are free, first evicts (n - free) tokens; if still short, RS_E_NOSPACE: nothing is
+ * allocated, and what was evicted stays evicted [L "Worked example"]. */
+int rs_alloc_slots(rs_tree* t, int64_t n, int32_t* out_slots);
+
+/* Return slots that were allocated and never inserted.  Freeing a free slot is RS_E_INVAL. */
+int rs_free_slots(rs_tree* t, const int32_t* slots, int64_t n);
+
+/* Insert tokens[0..n) with slots[0..n) (host, in/out) [L step 4].  Splits at the
+ * divergence point like match.  Positions already in the tree keep the tree's slots:
+ * a caller slot that differs is freed and overwritten with the tree's.  The rest,
+ * slots[prefix..n), is adopted by one new leaf.  Returns the count already present
+ * in *out_prefix_len and the node the sequence ends at in *out_node. */
+int rs_insert(rs_tree* t, const int32_t* tokens, int32_t* slots, int64_t n,
+              int64_t* out_prefix_len, int64_t* out_node);
+
+/* Evict whole unlocked leaves, least (priority, last_access, node id) first, pushing a
+ * parent that becomes childless and unlocked, until num_tokens are freed or nothing is
+ * evictable [T][B "Eviction on a tree"][L].  Returns tokens freed (may exceed num_tokens). */
+int64_t rs_evict(rs_tree* t, int64_t num_tokens);
+
+/* One request's admission [L "What happens when a request arrives"]: match
+ * tokens[0..cached) and lock that node; allocate slots for the unmatched part of the
+ * cached tokens (to be re-prefilled), insert them and move the lock to the node the
+ * cached tokens end at; allocate n_new slots for the tokens this step computes.
+ * out_row (host, capacity cached + n_new) receives the request's index-table row.
+ * *out_node = the locked node; *out_matched = tokens matched (positions
+ * matched..cached+n_new-1 need their KV written).  On RS_E_NOSPACE the request holds
+ * no lock and no slots; tokens it already inserted stay cached. */
+int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new,
+             int32_t* out_row, int64_t* out_node, int64_t* out_matched);
+
+int rs_stats(const rs_tree* t, rs_stats_t* out);
+
+/* Canonical text of the tree (for tests): depth-first from the root, children in
+ * ascending first-token order, one line per node
+ * "depth id lock_ref last_access len | key tokens | slots\n".
+ * Writes at most cap bytes (NUL-terminated if room) and the full size (excluding
+ * the NUL) to *need. */
+int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need);
+
+/* ------------------------------------------------------------------ decode plan */
+
+/* Segments of a decode batch from the tree [L "How the runtime and frontend work
+ * together": forked requests reach the runtime as near-identical requests and their
+ * common part is computed once].  Request b (table row b) holds a lock on nodes[b],
+ * whose root path covers positions 0..cached_lens[b]-1; seq_lens[b] >= cached_lens[b]
+ * is its context including the new token(s).  A tree node on the paths of >= 2
+ * requests becomes a shared segment (a parent-child chain with one request set is one
+ * segment); the rest of each request, up to seq_lens[b], is its unique tail.  Segments
+ * are cut into key chunks and row tiles (<= 128 query rows = requests x Hq/Hkv) that
+ * form the work items of rs_decode_attention.  The plan only reads the tree. */
+int rs_decode_plan_build(const rs_tree* t, const int64_t* nodes, const int32_t* cached_lens,
+                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                         rs_plan** out);
+int rs_plan_info(const rs_plan* p, rs_plan_info_t* out);
+/* Size of the plan's device image; rs_decode_plan_upload copies it to dev (device,
+ * >= that many bytes, 16-byte aligned) on stream.  The plan must stay alive until
+ * the copy is done. */
+int64_t rs_decode_plan_bytes(const rs_plan* p);
+int rs_decode_plan_upload(const rs_plan* p, void* dev, void* stream);
+/* Copy the device image into host memory (bytes >= rs_decode_plan_bytes), for inspection.
+ * int32 words: header[16] = {magic, n_items, B, G, n_partials, off_items, off_item_req,
+ * off_part_ptr, off_part_list, 0...}; items[n_items][8] = {k0, k1, rep_row, n_req,
+ * req_off, part_base, 0, 0} (keys k0..k1-1 of table row rep_row, requests
+ * item_req[req_off..+n_req), partials part_base..+n_req); item_req[]; part_ptr[B+1];
+ * part_list[] (CSR: the partials of request b). */
+int rs_decode_plan_read(const rs_plan* p, void* host, int64_t bytes);
+void rs_plan_destroy(rs_plan* p);
+
+/* Workspace bytes rs_decode_attention needs: partial results plus one completion
+ * counter per (request, KV head).  plan = NULL sizes the flat (one segment per
+ * request) mode for B requests of up to max_seq_len tokens. */
+int64_t rs_decode_workspace_bytes(const rs_plan* p, int32_t B, int32_t max_seq_len,
+                                  int32_t Hq, int32_t Hkv, int32_t D);
+/* Zero a workspace before its first use (a fill kernel on stream).  The decode kernel
+ * leaves the counters at zero when it finishes, so one init serves any number of
+ * launches that use the workspace one after another. */
+int rs_decode_workspace_init(void* ws, int64_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ device ops */
+
+/* Write the K/V rows of n new tokens into their pool slots [L "A quick recap": the new
+ * token's keys and values are appended].  k_new, v_new: device [n][Hkv][D]; slots:
+ * device int32 [n], each in [0, pool_slots).  Pools: device [pool_slots][Hkv][D]. */
+int rs_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                const int32_t* slots, int64_t n, int32_t Hkv, int32_t D, int32_t dtype,
+                void* stream);
+
+/* Extend attention [L step 3: prefill only the unmatched suffix, attending to the
+ * reused KV as if just computed]: for request b, query i (0 <= i < extend_lens[b]) sits
+ * at position p = prefix_lens[b] + i and attends causally to positions 0..p, whose K/V
+ * rows are k_pool/v_pool[req_to_token[b*ld + j]]:
+ *   out[q, h] = softmax_j(sm_scale * q[q, h] . K[j, h/G]) V[j, h/G].
+ * q, out: device [sum(extend_lens)][Hq][D], requests packed in order (qo_indptr, device
+ * int32 [B+1], gives each request's first query row).  prefix_lens, extend_lens: device
+ * int32 [B]; req_to_token: device int32 [B][ld] with prefix+extend <= ld.
+ * max_extend_len (host) bounds extend_lens and sizes the grid.  bf16: MFMA with fp32
+ * accumulation; fp32: fp32 throughout. */
+int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,
+                        const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B,
+                        int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
+                        int32_t dtype, void* out, void* stream);
+
+/* Decode attention: one query per request at position seq_lens[b]-1 over positions
+ * 0..seq_lens[b]-1 (its own KV stored first) [L "A quick recap"].  q, out: device
+ * [B][Hq][D]; lse_out: device float [B][Hq] natural-log log-sum-exp, or NULL.
+ * With a plan (host handle `plan` and its uploaded image `plan_dev`), a shared segment
+ * is read once for all its requests as one multi-query tile; every work item writes a
+ * partial (o, lse) and the last item to finish for a (request, KV head) merges them:
+ *   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
+ * plan = NULL: each request is one segment (flat).  ws: device workspace of at least
+ * rs_decode_workspace_bytes, zeroed once by rs_decode_workspace_init.  Launches that
+ * share a workspace must not overlap.  fp32 runs the flat path (plan ignored). */
+int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                        int32_t B, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D,
+                        float sm_scale, int32_t dtype, const rs_plan* plan, const void* plan_dev,
+                        void* ws, int64_t ws_bytes, void* out, float* lse_out, void* stream);
+
+/* Merge two attention states over disjoint key sets (the combine step above), rows x D:
+ * o_a, o_b, o: device [rows][D] of dtype; lse_*: device float [rows]. */
+int rs_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    int64_t rows, int32_t D, int32_t dtype, void* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_H_ */

@@ -1,0 +1,102 @@
+"""RadixAttention's data-parallel hot path on one MI355X.
+
+A host radix tree (C++) indexes one token-granular KV pool; hand-written HIP
+kernels for gfx950 run extend and prefix-aware decode attention through the
+tree's index tables.  Everything crosses the C ABI in include/rs.h; this
+package only marshals torch tensors and numpy arrays into those calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (Tree, Plan, RsError, NoSpaceError, StaleError, DTYPE_F32, DTYPE_BF16,  # noqa: F401
+                   decode_workspace_bytes, LIB_PATH)
+
+__all__ = ["Tree", "Plan", "RsError", "NoSpaceError", "StaleError", "store_kv", "extend_attention",
+           "decode_attention", "merge_states", "DecodeWorkspace", "LIB_PATH"]
+
+_DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise RsError(_lib.RS_E_UNSUPPORTED, f"dtype {t.dtype} (float32 and bfloat16 are implemented)")
+    return _DT[t.dtype]
+
+
+def _stream(stream):
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise RsError(_lib.RS_E_INVAL, f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise RsError(_lib.RS_E_INVAL, f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def store_kv(k_pool, v_pool, k_new, v_new, slots, stream=None):
+    """k_pool/v_pool [S, Hkv, D]; k_new/v_new [n, Hkv, D]; slots int32 [n] (device)."""
+    S, Hkv, D = k_pool.shape
+    _lib.store_kv(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype), _dev(k_new, "k_new", k_pool.dtype),
+                  _dev(v_new, "v_new", k_pool.dtype), _dev(slots, "slots", torch.int32), slots.numel(), Hkv, D,
+                  _dtype(k_pool), _stream(stream))
+
+
+def extend_attention(q, k_pool, v_pool, req_to_token, qo_indptr, prefix_lens, extend_lens, max_extend_len,
+                     sm_scale, out=None, stream=None):
+    """q [sum(ext), Hq, D]; req_to_token int32 [B, ld]; qo_indptr [B+1], prefix_lens/extend_lens [B] (device)."""
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    B, ld = req_to_token.shape
+    out = torch.empty_like(q) if out is None else out
+    _lib.extend_attention(_dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+                          _dev(req_to_token, "req_to_token", torch.int32), ld,
+                          _dev(qo_indptr, "qo_indptr", torch.int32), _dev(prefix_lens, "prefix_lens", torch.int32),
+                          _dev(extend_lens, "extend_lens", torch.int32), B, max_extend_len, Hq, Hkv, D, sm_scale,
+                          _dtype(k_pool), _dev(out, "out", k_pool.dtype), _stream(stream))
+    return out
+
+
+class DecodeWorkspace:
+    """Device workspace for rs_decode_attention (partials + completion counters), zeroed once."""
+
+    def __init__(self, plan, B, max_seq_len, Hq, Hkv, D, device="cuda", stream=None):
+        self.nbytes = decode_workspace_bytes(plan, B, max_seq_len, Hq, Hkv, D)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        _lib.decode_workspace_init(self.buf.data_ptr(), self.nbytes, _stream(stream))
+
+
+def upload_plan(plan: Plan, device="cuda", stream=None):
+    """Device image of a plan (uint8 tensor); the plan must outlive the copy."""
+    dev = torch.empty(plan.nbytes, dtype=torch.uint8, device=device)
+    plan.upload(dev.data_ptr(), _stream(stream))
+    return dev
+
+
+def decode_attention(q, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, workspace, plan=None,
+                     plan_dev=None, out=None, lse=None, stream=None):
+    """q [B, Hq, D]; req_to_token int32 [B, ld]; seq_lens int32 [B] (device).  Returns out (and fills lse)."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    ld = req_to_token.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    _lib.decode_attention(_dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+                          _dev(req_to_token, "req_to_token", torch.int32), ld, _dev(seq_lens, "seq_lens", torch.int32),
+                          B, max_seq_len, Hq, Hkv, D, sm_scale, _dtype(k_pool), plan,
+                          plan_dev.data_ptr() if plan_dev is not None else None,
+                          workspace.buf.data_ptr(), workspace.nbytes, _dev(out, "out", k_pool.dtype),
+                          _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(stream))
+    return out
+
+
+def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse=None, stream=None):
+    """o_* [rows, D] (float32 or bfloat16), lse_* float32 [rows]."""
+    rows, D = o_a.shape
+    out = torch.empty_like(o_a) if out is None else out
+    _lib.merge_states(_dev(o_a, "o_a"), _dev(lse_a, "lse_a", torch.float32), _dev(o_b, "o_b", o_a.dtype),
+                      _dev(lse_b, "lse_b", torch.float32), rows, D, _dtype(o_a), _dev(out, "out", o_a.dtype),
+                      _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(stream))
+    return out

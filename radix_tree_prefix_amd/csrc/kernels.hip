@@ -1,0 +1,779 @@
+// Device ops of librs for gfx950 (CDNA4): KV store, extend attention, prefix-aware
+// decode attention, log-sum-exp merge.
+//
+// The attention computed is causal softmax attention over each request's context,
+// reached through its index-table row ("How does SGLang work",
+// modernaiengineering.com: "A quick recap ..." -- a token's KV depends only on its
+// prefix and decode appends its own KV; "What happens when a request arrives" --
+// the unmatched suffix is prefilled attending to the reused KV as if it had just
+// been computed).
+//
+// bf16 tile engine (extend and decode share it).  A workgroup is 4 waves; each wave
+// owns up to 32 query rows (rows = tokens x heads of one KV-head group in extend,
+// requests x heads in decode).  Per 64-key tile the workgroup gathers the K rows
+// (row-major) and the V rows (transposed, keys permuted) through the index table
+// into LDS, then each wave runs, on 32x32x16 bf16 MFMAs:
+//     S^T[key][row] = K[key][:] . Q[row][:]      (A = K from LDS, B = Q^T in VGPRs)
+//     O^T[d][row]  += V^T[d][key] . P^T[key][row] (A = V^T from LDS, B = P^T in VGPRs)
+// With S^T in the accumulator a lane holds 32 scores of one query row (its partner
+// lane l^32 holds the other 32), so the online-softmax max/sum/rescale is lane-local
+// plus one cross-half exchange, and P^T feeds the second MFMA from the same registers
+// with no shuffle: the permuted key order of V^T in LDS matches the accumulator
+// layout.  fp32 runs a VALU path (one wave per query row).
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "internal.h"
+#include "plan.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kBN = 64;       // keys per LDS tile
+constexpr int kKPad = 8;      // bf16 padding per K row in LDS
+constexpr int kVPad = 8;      // bf16 padding per V^T row in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
+
+template <int D>
+struct __align__(16) Tile {
+  uint16_t k[kBN][D + kKPad];
+  uint16_t vt[D][kBN + kVPad];
+};
+
+// ------------------------------------------------------------------ tile loads
+// Per-thread staging registers for one K/V tile.
+template <int D>
+struct Stage {
+  static constexpr int kChunksPerRow = D / 8;                          // 16-byte chunks
+  static constexpr int kK = kBN * kChunksPerRow / kThreads;            // K chunks per thread
+  static constexpr int kLanesPerRow = D / 2;                           // dwords per V row
+  static constexpr int kRowsPerWaveLoad = 64 / kLanesPerRow;           // 1 (D=128) or 2 (D=64)
+  static constexpr int kVBlocks = 8 / (4 * kRowsPerWaveLoad);          // 8-key blocks per thread
+  uint4 k[kK];
+  uint32_t v[kVBlocks][8];
+};
+
+// Keys of the 8-key block kb (0..7) in the permuted V^T order: LDS positions kb*8+i hold
+// key 16*(kb/2) + 8*(i/4) + 4*(kb%2) + i%4.  That order makes P^T's rows (straight from
+// the S^T accumulator) and V^T's columns pair up in the PV MFMA.
+__device__ __forceinline__ int vkey(int kb, int i) { return 16 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3); }
+
+template <int D>
+__device__ __forceinline__ void load_tile(Stage<D>& st, const uint16_t* __restrict__ kp,
+                                          const uint16_t* __restrict__ vp, const int32_t* __restrict__ trow,
+                                          int key0, int nk, int64_t slot_stride, int tid) {
+  using S = Stage<D>;
+#pragma unroll
+  for (int i = 0; i < S::kK; ++i) {
+    int c = tid + i * kThreads;
+    int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
+    if (row < nk) {
+      int64_t slot = trow[key0 + row];
+      st.k[i] = *reinterpret_cast<const uint4*>(kp + slot * slot_stride + ch * 8);
+    } else {
+      st.k[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int sub = lane / S::kLanesPerRow, dw = lane % S::kLanesPerRow;
+#pragma unroll
+  for (int blk = 0; blk < S::kVBlocks; ++blk) {
+    int kb = (blk * 4 + wave) * S::kRowsPerWaveLoad + sub;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int key = vkey(kb, i);
+      if (key < nk) {
+        int64_t slot = trow[key0 + key];
+        st.v[blk][i] = *reinterpret_cast<const uint32_t*>(vp + slot * slot_stride + 2 * dw);
+      } else {
+        st.v[blk][i] = 0u;
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(Tile<D>& sm, const Stage<D>& st, int tid) {
+  using S = Stage<D>;
+#pragma unroll
+  for (int i = 0; i < S::kK; ++i) {
+    int c = tid + i * kThreads;
+    int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
+    *reinterpret_cast<uint4*>(&sm.k[row][ch * 8]) = st.k[i];
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int sub = lane / S::kLanesPerRow, dw = lane % S::kLanesPerRow;
+#pragma unroll
+  for (int blk = 0; blk < S::kVBlocks; ++blk) {
+    int kb = (blk * 4 + wave) * S::kRowsPerWaveLoad + sub;
+    const uint32_t* v = st.v[blk];
+    uint4 lo, hi;   // d = 2*dw (low halves) and d = 2*dw+1 (high halves) for the 8 keys
+    lo.x = (v[0] & 0xffffu) | (v[1] << 16);
+    lo.y = (v[2] & 0xffffu) | (v[3] << 16);
+    lo.z = (v[4] & 0xffffu) | (v[5] << 16);
+    lo.w = (v[6] & 0xffffu) | (v[7] << 16);
+    hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
+    hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
+    hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
+    hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
+    *reinterpret_cast<uint4*>(&sm.vt[2 * dw][kb * 8]) = lo;
+    *reinterpret_cast<uint4*>(&sm.vt[2 * dw + 1][kb * 8]) = hi;
+  }
+}
+
+// ------------------------------------------------------------------ per-wave math
+// Online-softmax state of one wave: lane l owns query row l%32 (shared with lane l^32).
+template <int D>
+struct WaveState {
+  f32x16 o[D / 32];     // O^T accumulators: o[mb][j] = O[row][mb*32 + 8*(j/4) + 4*(lane/32) + j%4]
+  float m;              // running max of raw scores (-inf before any visible key)
+  float l;              // this lane's half of the running sum of exp2((s - m) * c)
+};
+
+template <int D>
+__device__ __forceinline__ void wave_init(WaveState<D>& ws) {
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ws.o[mb][j] = 0.f;
+  ws.m = -INFINITY;
+  ws.l = 0.f;
+}
+
+// Query fragments (B operand of S^T): qf[ks] = Q[row][16*ks + 8*(lane/32) .. +8].
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t* __restrict__ qrow, bool valid,
+                                       int lane) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * (lane >> 5)) : make_uint4(0, 0, 0, 0);
+    qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+// One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
+// visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
+template <int D, bool MASK>
+__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Tile<D>& sm, const bf16x8 (&qf)[D / 16],
+                                          int lane, int nk, int key_pos0, int lim, float c) {
+  const int r32 = lane & 31, hi = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[kb * 32 + r32][16 * ks + 8 * hi]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+    }
+  }
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        int t = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        if (t >= nk || key_pos0 + t > lim) s[kb][j] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(ws.m, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = exp2f((ws.m - m_use) * c);
+  const float mc = m_use * c;
+  float sum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float p = exp2f(fmaf(s[kb][j], c, -mc));
+      s[kb][j] = p;
+      sum += p;
+    }
+  ws.l = fmaf(ws.l, alpha, sum);
+  ws.m = m_new;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ws.o[mb][j] *= alpha;
+#pragma unroll
+  for (int kstep = 0; kstep < 4; ++kstep) {
+    const int kb = kstep >> 1, h8 = (kstep & 1) * 8;
+    uint4 pu;
+    pu.x = pack_bf16(s[kb][h8 + 0], s[kb][h8 + 1]);
+    pu.y = pack_bf16(s[kb][h8 + 2], s[kb][h8 + 3]);
+    pu.z = pack_bf16(s[kb][h8 + 4], s[kb][h8 + 5]);
+    pu.w = pack_bf16(s[kb][h8 + 6], s[kb][h8 + 7]);
+    bf16x8 b = __builtin_bit_cast(bf16x8, pu);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[mb * 32 + r32][16 * kstep + 8 * hi]);
+      ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
+    }
+  }
+}
+
+// Stream keys [k0, k1) of one index-table row through the workgroup.  Waves with
+// has_rows run the math; every wave helps load.  mask_from: first key position at
+// which any row of the workgroup may need masking (keys >= k1 are always masked).
+template <int D>
+__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Tile<D>& sm, const bf16x8 (&qf)[D / 16],
+                                            const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+                                            const int32_t* __restrict__ trow, int64_t slot_stride, int k0, int k1,
+                                            int mask_from, int lim, float c, bool has_rows, int tid) {
+  const int lane = tid & 63;
+  Stage<D> st;
+  if (k0 >= k1) return;
+  load_tile<D>(st, kp, vp, trow, k0, min(kBN, k1 - k0), slot_stride, tid);
+  for (int key0 = k0; key0 < k1; key0 += kBN) {
+    const int nk = min(kBN, k1 - key0);
+    __syncthreads();                      // previous tile fully consumed
+    store_tile<D>(sm, st, tid);
+    __syncthreads();
+    if (key0 + kBN < k1) load_tile<D>(st, kp, vp, trow, key0 + kBN, min(kBN, k1 - key0 - kBN), slot_stride, tid);
+    if (has_rows) {
+      if (nk == kBN && key0 + kBN <= mask_from) wave_tile<D, false>(ws, sm, qf, lane, nk, key0, lim, c);
+      else wave_tile<D, true>(ws, sm, qf, lane, nk, key0, lim, c);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ extend (bf16)
+template <int D>
+__global__ void __launch_bounds__(kThreads) extend_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
+    int Hkv, float sm_scale, uint16_t* __restrict__ out) {
+  __shared__ Tile<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = Hq / Hkv;
+  const int tpb = 128 / G;                        // tokens per tile
+  const int kvh = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int qt = rest % n_qtiles, b = rest / n_qtiles;
+  const int ext = extend_lens[b];
+  const int t0 = qt * tpb;
+  if (t0 >= ext) return;
+  const int prefix = prefix_lens[b];
+  const int qo = qo_indptr[b];
+  const int ntok = min(tpb, ext - t0);
+  const int row = wave * 32 + (lane & 31);
+  const int t = row / G, g = row % G;
+  const bool valid = row < tpb * G && t < ntok;
+  const int64_t qrow_idx = int64_t(qo + t0 + t) * Hq + kvh * G + g;
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, q + qrow_idx * D, valid, lane);
+  WaveState<D> ws;
+  wave_init<D>(ws);
+  const int lim = valid ? prefix + t0 + t : -1;
+  const int key_end = prefix + t0 + ntok;
+  const int mask_from = prefix + t0 + 1;          // keys below this are visible to every row
+  const bool has_rows = wave * 32 < ntok * G;
+  const float c = sm_scale * kLog2e;
+  stream_keys<D>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
+                 int64_t(Hkv) * D, 0, key_end, mask_from, lim, c, has_rows, tid);
+  if (!valid) return;
+  float l = ws.l + __shfl_xor(ws.l, 32);
+  float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = out + qrow_idx * D;
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      int d = mb * 32 + 8 * q4 + 4 * hi;
+      uint2 u;
+      u.x = pack_bf16(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv);
+      u.y = pack_bf16(ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + d) = u;
+    }
+}
+
+// ------------------------------------------------------------------ decode (bf16)
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  const int32_t* req_to_token;
+  int64_t ld;
+  const int32_t* seq_lens;
+  const int32_t* plan;        // device image, or nullptr for the flat mode
+  int flat_nch;               // flat mode: chunks per request
+  int Hq, Hkv;
+  float sm_scale;
+  float* o_part;              // [Hkv][P][G][D]
+  float* lse_part;            // [Hkv][P][G]
+  int* cnt;                   // [B][Hkv]
+  int64_t n_partials;
+  uint16_t* out;              // [B][Hq][D]
+  float* lse_out;             // [B][Hq] or nullptr
+};
+
+// Partials of request b: count and the i-th partial index.
+struct PartList {
+  const int32_t* list;
+  int base, n;
+  __device__ int at(int i) const { return list ? list[i] : base + i; }
+};
+
+template <int D>
+__device__ void merge_request(const DecodeArgs& a, int b, int kvh, const PartList& pl, int tid) {
+  const int G = a.Hq / a.Hkv;
+  const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
+  const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int g = e / D, d = e % D;
+    float mx = -INFINITY;
+    for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g]);
+    float wsum = 0.f, acc = 0.f;
+    for (int i = 0; i < pl.n; ++i) {
+      const int64_t p = pl.at(i);
+      const float w = __expf(lp[p * G + g] - mx);
+      wsum += w;
+      acc = fmaf(w, op[(p * G + g) * D + d], acc);
+    }
+    const int64_t orow = int64_t(b) * a.Hq + kvh * G + g;
+    a.out[orow * D + d] = f2bf(acc / wsum);
+    if (d == 0 && a.lse_out) a.lse_out[orow] = mx + __logf(wsum);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) decode_bf16_kernel(DecodeArgs a) {
+  __shared__ Tile<D> sm;
+  __shared__ int s_req[rs::kMaxRowsPerItem];
+  __shared__ int s_last[rs::kMaxRowsPerItem];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.Hq / a.Hkv;
+  const int kvh = blockIdx.x % a.Hkv;
+  const int item = blockIdx.x / a.Hkv;
+  int k0, k1, rep, nreq, req_off = 0, part_base;
+  if (a.plan) {
+    const int32_t* it = a.plan + a.plan[5] + item * rs::kItemWords;
+    k0 = it[0]; k1 = it[1]; rep = it[2]; nreq = it[3]; req_off = it[4]; part_base = it[5];
+  } else {
+    const int b = item / a.flat_nch, ch = item % a.flat_nch;
+    k0 = ch * rs::kFlatChunk;
+    k1 = min(k0 + rs::kFlatChunk, a.seq_lens[b]);
+    if (k0 >= k1) return;
+    rep = b; nreq = 1; part_base = item;
+  }
+  const int32_t* item_req = a.plan ? a.plan + a.plan[6] + req_off : nullptr;
+  const int row = wave * 32 + (lane & 31);
+  const int j = row / G, g = row % G;
+  const bool valid = j < nreq;
+  const int b = valid ? (item_req ? item_req[j] : rep) : 0;
+  const int64_t qrow_idx = int64_t(b) * a.Hq + kvh * G + g;
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, a.q + qrow_idx * D, valid, lane);
+  WaveState<D> ws;
+  wave_init<D>(ws);
+  const bool has_rows = wave * 32 < nreq * G;
+  stream_keys<D>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
+                 a.req_to_token + int64_t(rep) * a.ld, int64_t(a.Hkv) * D, k0, k1, k1, INT32_MAX,
+                 a.sm_scale * kLog2e, has_rows, tid);
+
+  // partial count of each request of this item
+  int npart = 0;
+  PartList pl{nullptr, 0, 0};
+  if (valid) {
+    if (a.plan) {
+      const int32_t* pp = a.plan + a.plan[7];
+      pl.list = a.plan + a.plan[8] + pp[b];
+      pl.n = pp[b + 1] - pp[b];
+    } else {
+      pl.base = b * a.flat_nch;
+      pl.n = (a.seq_lens[b] + rs::kFlatChunk - 1) / rs::kFlatChunk;
+    }
+    npart = pl.n;
+  }
+  const float l = ws.l + __shfl_xor(ws.l, 32);
+  const int hi = lane >> 5;
+  if (valid) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (npart == 1) {                    // this item covers the request: final output
+      uint16_t* orow = a.out + qrow_idx * D;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int d = mb * 32 + 8 * q4 + 4 * hi;
+          uint2 u;
+          u.x = pack_bf16(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv);
+          u.y = pack_bf16(ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = u;
+        }
+      if (hi == 0 && a.lse_out) a.lse_out[qrow_idx] = ws.m * a.sm_scale + __logf(l);
+    } else {
+      const int64_t p = part_base + j;
+      float* orow = a.o_part + ((int64_t(kvh) * a.n_partials + p) * G + g) * D;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int d = mb * 32 + 8 * q4 + 4 * hi;
+          float4 v = make_float4(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv,
+                                 ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
+          *reinterpret_cast<float4*>(orow + d) = v;
+        }
+      if (hi == 0) a.lse_part[(int64_t(kvh) * a.n_partials + p) * G + g] = ws.m * a.sm_scale + __logf(l);
+    }
+  }
+  // completion: the last item to finish a (request, KV head) merges its partials
+  __threadfence();
+  __syncthreads();
+  if (tid < nreq) {
+    const int bb = item_req ? item_req[tid] : rep;
+    int n;
+    if (a.plan) {
+      const int32_t* pp = a.plan + a.plan[7];
+      n = pp[bb + 1] - pp[bb];
+    } else {
+      n = (a.seq_lens[bb] + rs::kFlatChunk - 1) / rs::kFlatChunk;
+    }
+    int last = 0;
+    if (n > 1) {
+      int old = __hip_atomic_fetch_add(&a.cnt[int64_t(bb) * a.Hkv + kvh], 1, __ATOMIC_ACQ_REL,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      last = (old == n - 1);
+    }
+    s_req[tid] = bb;
+    s_last[tid] = last;
+  }
+  __syncthreads();
+  for (int r = 0; r < nreq; ++r) {
+    if (!s_last[r]) continue;
+    __threadfence();
+    const int bb = s_req[r];
+    PartList q;
+    if (a.plan) {
+      const int32_t* pp = a.plan + a.plan[7];
+      q.list = a.plan + a.plan[8] + pp[bb];
+      q.base = 0;
+      q.n = pp[bb + 1] - pp[bb];
+    } else {
+      q.list = nullptr;
+      q.base = bb * a.flat_nch;
+      q.n = (a.seq_lens[bb] + rs::kFlatChunk - 1) / rs::kFlatChunk;
+    }
+    merge_request<D>(a, bb, kvh, q, tid);
+    if (tid == 0) a.cnt[int64_t(bb) * a.Hkv + kvh] = 0;     // ready for the next launch
+  }
+}
+
+// ------------------------------------------------------------------ fp32 (VALU)
+// One wave per (request, query, head).  Query rows come either from an extend batch
+// (qo_indptr / prefix_lens / extend_lens) or from a decode batch (seq_lens).
+template <int D>
+__global__ void __launch_bounds__(64) attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
+    const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens,
+    const int32_t* __restrict__ seq_lens, int max_q, int Hq, int Hkv, float sm_scale, float* __restrict__ out,
+    float* __restrict__ lse_out) {
+  constexpr int DPL = D / 64;                    // output dims per lane
+  __shared__ float qs[D];
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % Hq;
+  const int rest = blockIdx.x / Hq;
+  const int i = rest % max_q, b = rest / max_q;
+  int pos, qrow;
+  if (seq_lens) {
+    pos = seq_lens[b] - 1;
+    qrow = b;
+  } else {
+    if (i >= extend_lens[b]) return;
+    pos = prefix_lens[b] + i;
+    qrow = qo_indptr[b] + i;
+  }
+  const int G = Hq / Hkv, kvh = h / G;
+  const float* qp = q + (int64_t(qrow) * Hq + h) * D;
+  for (int d = lane; d < D; d += 64) qs[d] = qp[d];
+  __syncthreads();
+  const int32_t* trow = req_to_token + int64_t(b) * ld;
+  const int64_t stride = int64_t(Hkv) * D;
+  const float* kb = kpool + int64_t(kvh) * D;
+  const float* vb = vpool + int64_t(kvh) * D;
+  float m = -INFINITY, l = 0.f, o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  for (int key0 = 0; key0 <= pos; key0 += 64) {
+    const int key = key0 + lane;
+    const bool ok = key <= pos;
+    float s = -INFINITY;
+    int64_t slot = 0;
+    if (ok) {
+      slot = trow[key];
+      const float4* kr = reinterpret_cast<const float4*>(kb + slot * stride);
+      float acc = 0.f;
+#pragma unroll 4
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        float4 kv = kr[d4];
+        acc = fmaf(qs[4 * d4 + 0], kv.x, acc);
+        acc = fmaf(qs[4 * d4 + 1], kv.y, acc);
+        acc = fmaf(qs[4 * d4 + 2], kv.z, acc);
+        acc = fmaf(qs[4 * d4 + 3], kv.w, acc);
+      }
+      s = acc * sm_scale;
+    }
+    float mx = s;
+#pragma unroll
+    for (int off = 32; off; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __expf(m - m_new);
+    const float p = ok ? __expf(s - m_new) : 0.f;
+    float ps = p;
+#pragma unroll
+    for (int off = 32; off; off >>= 1) ps += __shfl_xor(ps, off);
+    l = l * alpha + ps;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] *= alpha;
+    const int nvalid = min(64, pos + 1 - key0);
+    for (int jj = 0; jj < nvalid; ++jj) {
+      const float pj = __shfl(p, jj);
+      const int64_t sj = __shfl(slot, jj);
+      const float* vr = vb + sj * stride;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] = fmaf(pj, vr[lane + 64 * k], o[k]);
+    }
+    m = m_new;
+  }
+  float* op = out + (int64_t(qrow) * Hq + h) * D;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) op[lane + 64 * k] = o[k] / l;
+  if (lse_out && lane == 0) lse_out[int64_t(qrow) * Hq + h] = m + logf(l);
+}
+
+// ------------------------------------------------------------------ small kernels
+__global__ void store_kv_kernel(uint4* __restrict__ kpool, uint4* __restrict__ vpool, const uint4* __restrict__ kn,
+                                const uint4* __restrict__ vn, const int32_t* __restrict__ slots, int64_t n,
+                                int row_chunks) {
+  const int64_t total = n * row_chunks;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = e / row_chunks, c = e % row_chunks;
+    const int64_t dst = int64_t(slots[r]) * row_chunks + c;
+    kpool[dst] = kn[e];
+    vpool[dst] = vn[e];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_as_f32<uint16_t>(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+__device__ __forceinline__ void st_from_f32(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_from_f32(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+
+template <typename T>
+__global__ void merge_states_kernel(const T* __restrict__ oa, const float* __restrict__ la, const T* __restrict__ ob,
+                                    const float* __restrict__ lb, int64_t rows, int D, T* __restrict__ o,
+                                    float* __restrict__ lse) {
+  const int64_t total = rows * D;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = e / D;
+    const float a = la[r], bb = lb[r];
+    const float mx = fmaxf(a, bb);
+    const float wa = __expf(a - mx), wb = __expf(bb - mx);
+    const float inv = 1.f / (wa + wb);
+    st_from_f32(o, e, (wa * ld_as_f32(oa, e) + wb * ld_as_f32(ob, e)) * inv);
+    if (lse && e % D == 0) lse[r] = mx + __logf(wa + wb);
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < n; e += int64_t(gridDim.x) * blockDim.x)
+    p[e] = 0u;
+}
+
+int grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  return int(std::min<int64_t>(std::max<int64_t>(g, 1), 65536));
+}
+
+int hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return rs::fail(RS_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return RS_OK;
+}
+
+bool dims_ok(int32_t Hq, int32_t Hkv, int32_t D) {
+  return Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq / Hkv <= rs::kMaxRowsPerItem && (D == 64 || D == 128);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI (device ops)
+extern "C" {
+
+int rs_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* slots, int64_t n,
+                int32_t Hkv, int32_t D, int32_t dtype, void* stream) {
+  if (n < 0 || Hkv <= 0 || D <= 0) return rs::fail(RS_E_INVAL, "rs_store_kv: bad sizes");
+  if (n == 0) return RS_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slots) return rs::fail(RS_E_INVAL, "rs_store_kv: null pointer");
+  if (dtype != RS_DTYPE_F32 && dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_store_kv: dtype");
+  const int64_t row_bytes = int64_t(Hkv) * D * (dtype == RS_DTYPE_F32 ? 4 : 2);
+  if (row_bytes % 16) return rs::fail(RS_E_UNSUPPORTED, "rs_store_kv: a KV row must be a multiple of 16 bytes");
+  for (const void* p : {static_cast<const void*>(k_pool), static_cast<const void*>(v_pool), k_new, v_new})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return rs::fail(RS_E_INVAL, "rs_store_kv: pointers must be 16-byte aligned");
+  const int rc = int(row_bytes / 16);
+  hipLaunchKernelGGL(store_kv_kernel, dim3(grid_for(n * rc, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), static_cast<const uint4*>(k_new),
+                     static_cast<const uint4*>(v_new), slots, n, rc);
+  return hip_check("rs_store_kv");
+}
+
+int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                        int64_t ld, const int32_t* qo_indptr, const int32_t* prefix_lens, const int32_t* extend_lens,
+                        int32_t B, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
+                        int32_t dtype, void* out, void* stream) {
+  if (B < 0 || max_extend_len < 0 || ld <= 0) return rs::fail(RS_E_INVAL, "rs_extend_attention: bad sizes");
+  if (!dims_ok(Hq, Hkv, D)) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: heads/head_dim unsupported");
+  if (B == 0 || max_extend_len == 0) return RS_OK;
+  if (!q || !k_pool || !v_pool || !req_to_token || !qo_indptr || !prefix_lens || !extend_lens || !out)
+    return rs::fail(RS_E_INVAL, "rs_extend_attention: null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == RS_DTYPE_BF16) {
+    const int G = Hq / Hkv, tpb = 128 / G;
+    const int n_qtiles = (max_extend_len + tpb - 1) / tpb;
+    const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
+    if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");
+    auto args = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+                         static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), req_to_token, ld,
+                         qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale,
+                         static_cast<uint16_t*>(out));
+    };
+    if (D == 128) args(extend_bf16_kernel<128>);
+    else args(extend_bf16_kernel<64>);
+    return hip_check("rs_extend_attention");
+  }
+  if (dtype == RS_DTYPE_F32) {
+    const int64_t blocks = int64_t(B) * max_extend_len * Hq;
+    if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");
+    auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64), 0, s, static_cast<const float*>(q),
+                       static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
+                       qo_indptr, prefix_lens, extend_lens, nullptr, max_extend_len, Hq, Hkv, sm_scale,
+                       static_cast<float*>(out), nullptr);
+    return hip_check("rs_extend_attention");
+  }
+  return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: dtype");
+}
+
+int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token, int64_t ld,
+                        const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D,
+                        float sm_scale, int32_t dtype, const rs_plan* plan, const void* plan_dev, void* ws,
+                        int64_t ws_bytes, void* out, float* lse_out, void* stream) {
+  if (B < 0 || max_seq_len < 0 || ld <= 0) return rs::fail(RS_E_INVAL, "rs_decode_attention: bad sizes");
+  if (!dims_ok(Hq, Hkv, D)) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: heads/head_dim unsupported");
+  if (B == 0) return RS_OK;
+  if (!q || !k_pool || !v_pool || !req_to_token || !seq_lens || !out)
+    return rs::fail(RS_E_INVAL, "rs_decode_attention: null pointer");
+  if (max_seq_len <= 0) return rs::fail(RS_E_INVAL, "rs_decode_attention: every request needs >= 1 key");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == RS_DTYPE_F32) {
+    auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(int64_t(B) * Hq)), dim3(64), 0, s, static_cast<const float*>(q),
+                       static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
+                       nullptr, nullptr, nullptr, seq_lens, 1, Hq, Hkv, sm_scale, static_cast<float*>(out), lse_out);
+    return hip_check("rs_decode_attention");
+  }
+  if (dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: dtype");
+  if ((plan == nullptr) != (plan_dev == nullptr))
+    return rs::fail(RS_E_INVAL, "rs_decode_attention: pass both the plan and its device image, or neither");
+  int64_t P, items;
+  int flat_nch = 0;
+  if (plan) {
+    const rs_plan_info_t* pi = rs::plan_info(plan);
+    if (pi->B != B || pi->Hq != Hq || pi->Hkv != Hkv || pi->D != D)
+      return rs::fail(RS_E_INVAL, "rs_decode_attention: batch or heads differ from the plan's");
+    P = pi->n_partials;
+    items = pi->n_items;
+  } else {
+    flat_nch = (max_seq_len + rs::kFlatChunk - 1) / rs::kFlatChunk;
+    P = int64_t(B) * flat_nch;
+    items = P;
+  }
+  const rs::WsLayout wl = rs::ws_layout(P, B, Hq, Hkv, D);
+  if (!ws || ws_bytes < wl.bytes)
+    return rs::fail(RS_E_INVAL, "rs_decode_attention: workspace smaller than rs_decode_workspace_bytes");
+  if (items * Hkv > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: grid too large");
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kpool = static_cast<const uint16_t*>(k_pool);
+  a.vpool = static_cast<const uint16_t*>(v_pool);
+  a.req_to_token = req_to_token;
+  a.ld = ld;
+  a.seq_lens = seq_lens;
+  a.plan = static_cast<const int32_t*>(plan_dev);
+  a.flat_nch = flat_nch;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.sm_scale = sm_scale;
+  char* w = static_cast<char*>(ws);
+  a.o_part = reinterpret_cast<float*>(w + wl.o_off);
+  a.lse_part = reinterpret_cast<float*>(w + wl.lse_off);
+  a.cnt = reinterpret_cast<int*>(w + wl.cnt_off);
+  a.n_partials = P;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse_out = lse_out;
+  if (D == 128) hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(unsigned(items * Hkv)), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(unsigned(items * Hkv)), dim3(kThreads), 0, s, a);
+  return hip_check("rs_decode_attention");
+}
+
+int rs_decode_workspace_init(void* ws, int64_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes <= 0 || (ws_bytes & 3) || (reinterpret_cast<uintptr_t>(ws) & 3))
+    return rs::fail(RS_E_INVAL, "rs_decode_workspace_init: bad workspace");
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(ws_bytes / 4, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(ws), ws_bytes / 4);
+  return hip_check("rs_decode_workspace_init");
+}
+
+int rs_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, int64_t rows, int32_t D,
+                    int32_t dtype, void* o, float* lse, void* stream) {
+  if (rows < 0 || D <= 0) return rs::fail(RS_E_INVAL, "rs_merge_states: bad sizes");
+  if (rows == 0) return RS_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return rs::fail(RS_E_INVAL, "rs_merge_states: null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = grid_for(rows * D, 256);
+  if (dtype == RS_DTYPE_F32)
+    hipLaunchKernelGGL(merge_states_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(o_a), lse_a,
+                       static_cast<const float*>(o_b), lse_b, rows, D, static_cast<float*>(o), lse);
+  else if (dtype == RS_DTYPE_BF16)
+    hipLaunchKernelGGL(merge_states_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(o_a),
+                       lse_a, static_cast<const uint16_t*>(o_b), lse_b, rows, D, static_cast<uint16_t*>(o), lse);
+  else
+    return rs::fail(RS_E_UNSUPPORTED, "rs_merge_states: dtype");
+  return hip_check("rs_merge_states");
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Constants and layouts shared by the decode-plan builder and the decode kernel.
+#pragma once
+
+#include <cstdint>
+
+#include "rs.h"
+
+namespace rs {
+
+constexpr int32_t kPlanMagic = 0x52535031;   // "RSP1"
+constexpr int32_t kPlanHeaderWords = 16;
+constexpr int32_t kItemWords = 8;            // k0, k1, rep_row, n_req, req_off, part_base, -, -
+constexpr int32_t kMaxRowsPerItem = 128;     // 4 waves x 32 query rows
+constexpr int32_t kFlatChunk = 256;          // keys per item in the flat (plan-less) mode
+constexpr int64_t kDecodeItemsTarget = 2048; // items x KV heads the chunk size aims for
+constexpr int64_t kMinChunk = 64;
+constexpr int64_t kMaxChunk = 8192;
+
+// Decode workspace: o partials float [Hkv][P][G][D], lse partials float [Hkv][P][G],
+// completion counters int32 [B][Hkv]; each region 256-byte aligned.
+struct WsLayout {
+  int64_t o_off, lse_off, cnt_off, bytes;
+};
+WsLayout ws_layout(int64_t n_partials, int32_t B, int32_t Hq, int32_t Hkv, int32_t D);
+const rs_plan_info_t* plan_info(const rs_plan* p);
+
+}  // namespace rs

@@ -1,0 +1,466 @@
+// Host radix tree over token prefixes, slot allocator and eviction.
+//
+// Follows "SGLang: the tree, and the language nobody remembers"
+// (ai.thesatyajit.com), section "A tree, not a map": nodes hold a token run,
+// one KV slot per token, children keyed on the first token (page size 1),
+// lock_ref, last access and priority; a node splits at the divergence point;
+// lock_ref changes move a node's tokens between the evictable and protected
+// totals on its 0<->1 edge; eviction pops unlocked leaves off a heap and
+// pushes a parent that the pop left childless and unlocked.  The edge compare
+// is a galloping search (doubling windows, then a binary search inside the
+// window that holds the divergence), which is what the same section describes
+// for long shared prefixes.  Request admission follows "How does SGLang work"
+// (modernaiengineering.com), "What happens when a request arrives".
+//
+// Where the pages leave a rule open the tree takes: a logical clock that ticks
+// once per match or insert call and stamps every node the call visits; heap
+// key (priority, last_access, id), priority 0 (pure least-recently-used, the
+// recency order the other pages describe); splits in match and in insert, the
+// upper part getting a fresh id and the lower part's lock_ref and last access;
+// lowest-free-first slots; on insert over present tokens the tree's slots win.
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <queue>
+#include <tuple>
+
+#include "internal.h"
+
+namespace rs {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+// Index of the first position where a and b differ (n if none).  Galloping:
+// windows [0,1), [1,3), [3,7), ... are compared whole; the first window that
+// differs is bisected with whole-span compares.
+static int64_t diverge(const int32_t* a, const int32_t* b, int64_t n) {
+  int64_t lo = 0, w = 1;
+  while (lo < n) {
+    int64_t len = std::min(w, n - lo);
+    if (std::memcmp(a + lo, b + lo, size_t(len) * 4) != 0) {
+      int64_t l = lo, r = lo + len;       // a[0..l) == b[0..l); they differ in [l, r)
+      while (r - l > 1) {
+        int64_t mid = l + (r - l) / 2;
+        if (std::memcmp(a + l, b + l, size_t(mid - l) * 4) == 0) l = mid;
+        else r = mid;
+      }
+      return l;
+    }
+    lo += len;
+    w *= 2;
+  }
+  return n;
+}
+
+SlotAllocator::SlotAllocator(int64_t n) : n_(n), nfree_(n), hint_(0), bits_((n + 63) / 64, ~0ull) {
+  if (n & 63) bits_.back() = (1ull << (n & 63)) - 1;
+}
+
+void SlotAllocator::take(int64_t k, int32_t* out) {
+  int64_t got = 0, w = hint_;
+  while (got < k) {
+    uint64_t b = bits_[w];
+    while (b && got < k) {
+      int tz = __builtin_ctzll(b);
+      out[got++] = int32_t(w * 64 + tz);
+      b &= b - 1;
+    }
+    bits_[w] = b;
+    if (!b) ++w;
+  }
+  hint_ = w;
+  nfree_ -= k;
+}
+
+bool SlotAllocator::give_back(const int32_t* s, int64_t k) {
+  for (int64_t i = 0; i < k; ++i) {
+    int32_t x = s[i];
+    bool bad = x < 0 || x >= n_ || is_free(x);
+    if (bad) {
+      for (int64_t j = 0; j < i; ++j) bits_[s[j] >> 6] &= ~(1ull << (s[j] & 63));
+      return false;
+    }
+    bits_[x >> 6] |= 1ull << (x & 63);
+  }
+  for (int64_t i = 0; i < k; ++i) hint_ = std::min<int64_t>(hint_, s[i] >> 6);
+  nfree_ += k;
+  return true;
+}
+
+}  // namespace rs
+
+using rs::Node;
+
+rs_tree::rs_tree(int64_t pool_slots) : alloc(pool_slots) { root.id = 0; }
+
+Node* rs_tree::find(int64_t id) {
+  if (id == 0) return &root;
+  auto it = nodes.find(id);
+  return it == nodes.end() ? nullptr : it->second.get();
+}
+const Node* rs_tree::find(int64_t id) const {
+  if (id == 0) return &root;
+  auto it = nodes.find(id);
+  return it == nodes.end() ? nullptr : it->second.get();
+}
+
+Node* rs_tree::split(Node* child, int64_t k) {
+  auto up = std::make_unique<Node>();
+  Node* u = up.get();
+  u->id = next_id++;
+  u->key.assign(child->key.begin(), child->key.begin() + k);
+  u->value.assign(child->value.begin(), child->value.begin() + k);
+  u->parent = child->parent;
+  u->lock_ref = child->lock_ref;
+  u->last_access = child->last_access;
+  u->priority = child->priority;
+  u->parent->children[child->key[0]] = u;
+  child->key.erase(child->key.begin(), child->key.begin() + k);
+  child->value.erase(child->value.begin(), child->value.begin() + k);
+  child->parent = u;
+  u->children[child->key[0]] = child;
+  nodes.emplace(u->id, std::move(up));
+  return u;
+}
+
+int64_t rs_tree::match(const int32_t* tok, int64_t n, int32_t* out, Node** end) {
+  ++clock;
+  ++match_calls;
+  Node* node = &root;
+  int64_t pos = 0;
+  while (pos < n) {
+    auto it = node->children.find(tok[pos]);
+    if (it == node->children.end()) break;
+    Node* c = it->second;
+    c->last_access = clock;
+    int64_t len = int64_t(c->key.size());
+    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos));
+    if (k < len) c = split(c, k);
+    if (out) std::memcpy(out + pos, c->value.data(), size_t(k) * 4);
+    pos += k;
+    node = c;
+  }
+  matched_total += pos;
+  *end = node;
+  return pos;
+}
+
+int rs_tree::insert(const int32_t* tok, int32_t* slots, int64_t n, int64_t* prefix, Node** end) {
+  for (int64_t i = 0; i < n; ++i)
+    if (slots[i] < 0 || slots[i] >= alloc.capacity() || alloc.is_free(slots[i]))
+      return rs::fail(RS_E_INVAL, "rs_insert: slot " + std::to_string(slots[i]) + " at position " +
+                                      std::to_string(i) + " is out of range or not allocated");
+  ++clock;
+  ++insert_calls;
+  Node* node = &root;
+  int64_t pos = 0;
+  int rc = RS_OK;
+  while (pos < n) {
+    auto it = node->children.find(tok[pos]);
+    if (it == node->children.end()) break;
+    Node* c = it->second;
+    c->last_access = clock;
+    int64_t len = int64_t(c->key.size());
+    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos));
+    if (k < len) c = split(c, k);
+    for (int64_t i = 0; i < k; ++i) {
+      int32_t& s = slots[pos + i];
+      if (s != c->value[i]) {
+        if (!alloc.give_back(&s, 1)) rc = rs::fail(RS_E_INVAL, "rs_insert: duplicate caller slot");
+        s = c->value[i];
+      }
+    }
+    pos += k;
+    node = c;
+  }
+  *prefix = pos;
+  if (pos < n) {
+    auto leaf = std::make_unique<Node>();
+    Node* l = leaf.get();
+    l->id = next_id++;
+    l->key.assign(tok + pos, tok + n);
+    l->value.assign(slots + pos, slots + n);
+    l->parent = node;
+    l->last_access = clock;
+    node->children[tok[pos]] = l;
+    nodes.emplace(l->id, std::move(leaf));
+    evictable += n - pos;
+    tree_tokens += n - pos;
+    node = l;
+  }
+  *end = node;
+  return rc;
+}
+
+void rs_tree::lock(Node* nd) {
+  for (; nd != &root; nd = nd->parent) {
+    if (nd->lock_ref == 0) {
+      evictable -= int64_t(nd->key.size());
+      protected_ += int64_t(nd->key.size());
+    }
+    ++nd->lock_ref;
+  }
+}
+
+int rs_tree::unlock(Node* nd) {
+  if (nd != &root && nd->lock_ref <= 0)
+    return rs::fail(RS_E_INVAL, "rs_dec_lock_ref: node " + std::to_string(nd->id) + " is not locked");
+  for (; nd != &root; nd = nd->parent) {
+    if (nd->lock_ref == 1) {
+      evictable += int64_t(nd->key.size());
+      protected_ -= int64_t(nd->key.size());
+    }
+    --nd->lock_ref;
+  }
+  return RS_OK;
+}
+
+int64_t rs_tree::evict(int64_t need) {
+  typedef std::tuple<int64_t, uint64_t, int64_t> Key;   // (priority, last_access, id)
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+  for (auto& kv : nodes) {
+    Node* n = kv.second.get();
+    if (n->children.empty() && n->lock_ref == 0) heap.emplace(n->priority, n->last_access, n->id);
+  }
+  int64_t freed = 0;
+  while (freed < need && !heap.empty()) {
+    int64_t id = std::get<2>(heap.top());
+    heap.pop();
+    Node* x = nodes[id].get();
+    int64_t len = int64_t(x->key.size());
+    alloc.give_back(x->value.data(), len);
+    freed += len;
+    evictable -= len;
+    tree_tokens -= len;
+    Node* p = x->parent;
+    p->children.erase(x->key[0]);
+    nodes.erase(id);
+    if (p != &root && p->children.empty() && p->lock_ref == 0)
+      heap.emplace(p->priority, p->last_access, p->id);
+  }
+  evicted_total += freed;
+  return freed;
+}
+
+int rs_tree::alloc_slots(int64_t n, int32_t* out) {
+  if (n < 0) return rs::fail(RS_E_INVAL, "rs_alloc_slots: negative count");
+  if (alloc.num_free() < n) {
+    evict(n - alloc.num_free());
+    if (alloc.num_free() < n)
+      return rs::fail(RS_E_NOSPACE, "rs_alloc_slots: " + std::to_string(n) + " slots wanted, " +
+                                        std::to_string(alloc.num_free()) +
+                                        " free after evicting every unlocked leaf");
+  }
+  alloc.take(n, out);
+  return RS_OK;
+}
+
+int64_t rs_tree::depth_tokens(const Node* nd) const {
+  int64_t d = 0;
+  for (; nd != &root; nd = nd->parent) d += int64_t(nd->key.size());
+  return d;
+}
+
+// ------------------------------------------------------------------ C ABI (tree)
+
+#define RS_GUARD_BEGIN try {
+#define RS_GUARD_END                                                    \
+  }                                                                     \
+  catch (const std::bad_alloc&) {                                       \
+    return rs::fail(RS_E_INVAL, "out of host memory");                  \
+  }                                                                     \
+  catch (const std::exception& e) {                                     \
+    return rs::fail(RS_E_INVAL, e.what());                              \
+  }
+
+extern "C" {
+
+const char* rs_last_error(void) { return rs::g_last_error.c_str(); }
+const char* rs_version(void) { return "librs 0.1 (gfx950)"; }
+
+rs_tree* rs_tree_create(int64_t pool_slots, int32_t page_size) {
+  if (pool_slots <= 0 || pool_slots > (int64_t(1) << 31) - 1) {
+    rs::set_error("rs_tree_create: pool_slots must be in [1, 2^31)");
+    return nullptr;
+  }
+  if (page_size != 1) {
+    rs::set_error("rs_tree_create: only page_size 1 (token-granular) is implemented");
+    return nullptr;
+  }
+  try {
+    return new rs_tree(pool_slots);
+  } catch (...) {
+    rs::set_error("rs_tree_create: out of host memory");
+    return nullptr;
+  }
+}
+
+void rs_tree_destroy(rs_tree* t) { delete t; }
+
+int rs_match_prefix(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_slots,
+                    int64_t* out_len, int64_t* out_node) {
+  if (!t || n < 0 || (n && (!tokens || !out_slots)) || !out_len || !out_node)
+    return rs::fail(RS_E_INVAL, "rs_match_prefix: bad arguments");
+  RS_GUARD_BEGIN
+  Node* end = nullptr;
+  *out_len = t->match(tokens, n, out_slots, &end);
+  *out_node = end->id;
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_inc_lock_ref(rs_tree* t, int64_t node) {
+  if (!t) return rs::fail(RS_E_INVAL, "rs_inc_lock_ref: null tree");
+  Node* n = t->find(node);
+  if (!n) return rs::fail(RS_E_STALE, "rs_inc_lock_ref: node " + std::to_string(node) + " is gone");
+  t->lock(n);
+  return RS_OK;
+}
+
+int rs_dec_lock_ref(rs_tree* t, int64_t node) {
+  if (!t) return rs::fail(RS_E_INVAL, "rs_dec_lock_ref: null tree");
+  Node* n = t->find(node);
+  if (!n) return rs::fail(RS_E_STALE, "rs_dec_lock_ref: node " + std::to_string(node) + " is gone");
+  return t->unlock(n);
+}
+
+int rs_alloc_slots(rs_tree* t, int64_t n, int32_t* out_slots) {
+  if (!t || n < 0 || (n && !out_slots)) return rs::fail(RS_E_INVAL, "rs_alloc_slots: bad arguments");
+  RS_GUARD_BEGIN
+  return t->alloc_slots(n, out_slots);
+  RS_GUARD_END
+}
+
+int rs_free_slots(rs_tree* t, const int32_t* slots, int64_t n) {
+  if (!t || n < 0 || (n && !slots)) return rs::fail(RS_E_INVAL, "rs_free_slots: bad arguments");
+  if (!t->alloc.give_back(slots, n))
+    return rs::fail(RS_E_INVAL, "rs_free_slots: a slot is out of range or already free");
+  return RS_OK;
+}
+
+int rs_insert(rs_tree* t, const int32_t* tokens, int32_t* slots, int64_t n, int64_t* out_prefix_len,
+              int64_t* out_node) {
+  if (!t || n < 0 || (n && (!tokens || !slots)) || !out_prefix_len || !out_node)
+    return rs::fail(RS_E_INVAL, "rs_insert: bad arguments");
+  RS_GUARD_BEGIN
+  Node* end = nullptr;
+  int64_t prefix = 0;
+  int rc = t->insert(tokens, slots, n, &prefix, &end);
+  if (end) {
+    *out_prefix_len = prefix;
+    *out_node = end->id;
+  }
+  return rc;
+  RS_GUARD_END
+}
+
+int64_t rs_evict(rs_tree* t, int64_t num_tokens) {
+  if (!t || num_tokens < 0) return rs::fail(RS_E_INVAL, "rs_evict: bad arguments");
+  RS_GUARD_BEGIN
+  return t->evict(num_tokens);
+  RS_GUARD_END
+}
+
+int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new, int32_t* out_row,
+             int64_t* out_node, int64_t* out_matched) {
+  if (!t || cached < 0 || n_new < 0 || (cached + n_new && (!tokens || !out_row)) || !out_node ||
+      !out_matched)
+    return rs::fail(RS_E_INVAL, "rs_admit: bad arguments");
+  RS_GUARD_BEGIN
+  Node* node = nullptr;
+  int64_t m = t->match(tokens, cached, out_row, &node);
+  t->lock(node);
+  if (cached > m) {
+    int rc = t->alloc_slots(cached - m, out_row + m);
+    if (rc != RS_OK) {
+      t->unlock(node);
+      return rc;
+    }
+    int64_t prefix = 0;
+    Node* node2 = nullptr;
+    rc = t->insert(tokens, out_row, cached, &prefix, &node2);
+    if (rc != RS_OK) {
+      t->unlock(node);
+      return rc;
+    }
+    t->lock(node2);
+    t->unlock(node);
+    node = node2;
+  }
+  if (n_new) {
+    int rc = t->alloc_slots(n_new, out_row + cached);
+    if (rc != RS_OK) {
+      t->unlock(node);
+      return rc;
+    }
+  }
+  *out_node = node->id;
+  *out_matched = m;
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_stats(const rs_tree* t, rs_stats_t* out) {
+  if (!t || !out) return rs::fail(RS_E_INVAL, "rs_stats: bad arguments");
+  std::memset(out, 0, sizeof(*out));
+  out->pool_slots = t->alloc.capacity();
+  out->nodes = int64_t(t->nodes.size());
+  out->tree_tokens = t->tree_tokens;
+  out->evictable = t->evictable;
+  out->protected_ = t->protected_;
+  out->free_slots = t->alloc.num_free();
+  out->evicted_total = t->evicted_total;
+  out->clock = int64_t(t->clock);
+  out->matched_total = t->matched_total;
+  out->match_calls = t->match_calls;
+  out->insert_calls = t->insert_calls;
+  return RS_OK;
+}
+
+int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need) {
+  if (!t || !need || cap < 0 || (cap && !buf)) return rs::fail(RS_E_INVAL, "rs_tree_dump: bad arguments");
+  RS_GUARD_BEGIN
+  std::string s;
+  char tmp[96];
+  // explicit stack: (node, depth); children pushed in descending first-token order
+  std::vector<std::pair<const Node*, int>> st;
+  auto push_children = [&](const Node* n, int depth) {
+    std::vector<int32_t> keys;
+    keys.reserve(n->children.size());
+    for (auto& kv : n->children) keys.push_back(kv.first);
+    std::sort(keys.begin(), keys.end());
+    for (auto it = keys.rbegin(); it != keys.rend(); ++it) st.emplace_back(n->children.at(*it), depth);
+  };
+  push_children(&t->root, 0);
+  while (!st.empty()) {
+    const Node* c = st.back().first;
+    int depth = st.back().second;
+    st.pop_back();
+    std::snprintf(tmp, sizeof tmp, "%d %lld %d %llu %zu |", depth, (long long)c->id, c->lock_ref,
+                  (unsigned long long)c->last_access, c->key.size());
+    s += tmp;
+    for (int32_t x : c->key) { s += ' '; s += std::to_string(x); }
+    s += " |";
+    for (int32_t x : c->value) { s += ' '; s += std::to_string(x); }
+    s += '\n';
+    push_children(c, depth + 1);
+  }
+  *need = int64_t(s.size());
+  if (cap > 0) {
+    int64_t k = std::min<int64_t>(cap - 1, int64_t(s.size()));
+    std::memcpy(buf, s.data(), size_t(k));
+    buf[k] = 0;
+  }
+  return RS_OK;
+  RS_GUARD_END
+}
+
+}  // extern "C"
