@@ -28,7 +28,7 @@ def admit(tree: RadixTree, tokens, cached: int, new: int):
     (re-prefill); so do positions cached..cached+new-1.
     """
     tokens = np.asarray(tokens, dtype=np.int32)
-    assert len(tokens) >= cached + new
+    assert len(tokens) >= cached
     got, node = tree.match_prefix(tokens[:cached])
     m = len(got)
     tree.inc_lock_ref(node)
