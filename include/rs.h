@@ -188,14 +188,13 @@ int rs_decode_plan_upload(const rs_plan* p, void* dev, void* stream);
 int rs_decode_plan_read(const rs_plan* p, void* host, int64_t bytes);
 void rs_plan_destroy(rs_plan* p);
 
-/* Workspace bytes rs_decode_attention needs: partial results plus one completion
- * counter per (request, KV head).  plan = NULL sizes the flat (one segment per
- * request) mode for B requests of up to max_seq_len tokens. */
+/* Workspace bytes rs_decode_attention needs: one partial (o, lse) per (work item,
+ * request, query head) in fp32.  plan = NULL sizes the flat (one segment per request)
+ * mode for B requests of up to max_seq_len tokens. */
 int64_t rs_decode_workspace_bytes(const rs_plan* p, int32_t B, int32_t max_seq_len,
                                   int32_t Hq, int32_t Hkv, int32_t D);
-/* Zero a workspace before its first use (a fill kernel on stream).  The decode kernel
- * leaves the counters at zero when it finishes, so one init serves any number of
- * launches that use the workspace one after another. */
+/* Zero a workspace (a fill kernel on stream).  Optional: every partial the merge reads
+ * is written first by the same rs_decode_attention call. */
 int rs_decode_workspace_init(void* ws, int64_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ device ops */
@@ -227,12 +226,13 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool,
  * 0..seq_lens[b]-1 (its own KV stored first) [L "A quick recap"].  q, out: device
  * [B][Hq][D]; lse_out: device float [B][Hq] natural-log log-sum-exp, or NULL.
  * With a plan (host handle `plan` and its uploaded image `plan_dev`), a shared segment
- * is read once for all its requests as one multi-query tile; every work item writes a
- * partial (o, lse) and the last item to finish for a (request, KV head) merges them:
+ * is read once for all its requests as one multi-query tile.  Every work item writes a
+ * partial (o, lse) to the workspace (or the final output when it alone covers a
+ * request) and a second kernel on the same stream merges each request's partials:
  *   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
  * plan = NULL: each request is one segment (flat).  ws: device workspace of at least
- * rs_decode_workspace_bytes, zeroed once by rs_decode_workspace_init.  Launches that
- * share a workspace must not overlap.  fp32 runs the flat path (plan ignored). */
+ * rs_decode_workspace_bytes.  Launches that share a workspace must not overlap.
+ * fp32 runs the flat path (plan ignored). */
 int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
                         int32_t B, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D,

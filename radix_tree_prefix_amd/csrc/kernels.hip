@@ -77,36 +77,41 @@ struct Stage {
 // the S^T accumulator) and V^T's columns pair up in the PV MFMA.
 __device__ __forceinline__ int vkey(int kb, int i) { return 16 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3); }
 
+// Slot ids of one tile: lane l of every wave holds the slot of key key0 + min(l, nk-1).
+// Keys past nk repeat the last valid slot (an in-bounds row); they are masked later.
+__device__ __forceinline__ int tile_slots(const int32_t* __restrict__ trow, int key0, int nk, int lane) {
+  return trow[key0 + min(lane, nk - 1)];
+}
+
+// Issue the global loads of one tile into the staging registers.  `sreg` is the tile's
+// slot register (tile_slots).  K: 16-byte chunks, the row's slot fetched from the lane
+// that holds it; V: one whole KV-head row per wave instruction (wave-uniform slot), so
+// the address is a scalar base plus the lane's dword offset.
 template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, const int32_t* __restrict__ trow,
-                                          int key0, int nk, int64_t slot_stride, int tid) {
+__device__ __forceinline__ void issue_tile(Stage<D>& st, const uint16_t* __restrict__ kp,
+                                           const uint16_t* __restrict__ vp, int sreg, uint32_t slot_stride,
+                                           int tid, int wave_u) {
   using S = Stage<D>;
 #pragma unroll
   for (int i = 0; i < S::kK; ++i) {
-    int c = tid + i * kThreads;
-    int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
-    if (row < nk) {
-      int64_t slot = trow[key0 + row];
-      st.k[i] = *reinterpret_cast<const uint4*>(kp + slot * slot_stride + ch * 8);
-    } else {
-      st.k[i] = make_uint4(0, 0, 0, 0);
-    }
+    const int c = tid + i * kThreads;
+    const int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
+    const uint32_t slot = uint32_t(__shfl(sreg, row));
+    st.k[i] = *reinterpret_cast<const uint4*>(kp + uint64_t(slot) * slot_stride + ch * 8);
   }
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
   const int sub = lane / S::kLanesPerRow, dw = lane % S::kLanesPerRow;
 #pragma unroll
   for (int blk = 0; blk < S::kVBlocks; ++blk) {
-    int kb = (blk * 4 + wave) * S::kRowsPerWaveLoad + sub;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      int key = vkey(kb, i);
-      if (key < nk) {
-        int64_t slot = trow[key0 + key];
-        st.v[blk][i] = *reinterpret_cast<const uint32_t*>(vp + slot * slot_stride + 2 * dw);
+      uint32_t slot;
+      if constexpr (S::kRowsPerWaveLoad == 1) {
+        slot = uint32_t(__builtin_amdgcn_readlane(sreg, vkey(blk * 4 + wave_u, i)));
       } else {
-        st.v[blk][i] = 0u;
+        slot = uint32_t(__shfl(sreg, vkey((blk * 4 + wave_u) * S::kRowsPerWaveLoad + sub, i)));
       }
+      st.v[blk][i] = *reinterpret_cast<const uint32_t*>(vp + uint64_t(slot) * slot_stride + 2 * dw);
     }
   }
 }
@@ -241,21 +246,34 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Tile<D>& sm, c
 // Stream keys [k0, k1) of one index-table row through the workgroup.  Waves with
 // has_rows run the math; every wave helps load.  mask_from: first key position at
 // which any row of the workgroup may need masking (keys >= k1 are always masked).
+// Pipeline: while tile t is computed from LDS, tile t+1's K/V loads and tile t+2's
+// slot ids are in flight.
 template <int D>
 __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Tile<D>& sm, const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-                                            const int32_t* __restrict__ trow, int64_t slot_stride, int k0, int k1,
+                                            const int32_t* __restrict__ trow, uint32_t slot_stride, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
-  const int lane = tid & 63;
-  Stage<D> st;
   if (k0 >= k1) return;
-  load_tile<D>(st, kp, vp, trow, k0, min(kBN, k1 - k0), slot_stride, tid);
-  for (int key0 = k0; key0 < k1; key0 += kBN) {
+  const int lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntiles = (k1 - k0 + kBN - 1) / kBN;
+  Stage<D> st;
+  int s_next = 0;
+  {
+    const int s0 = tile_slots(trow, k0, min(kBN, k1 - k0), lane);
+    if (ntiles > 1) s_next = tile_slots(trow, k0 + kBN, min(kBN, k1 - k0 - kBN), lane);
+    issue_tile<D>(st, kp, vp, s0, slot_stride, tid, wave_u);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int key0 = k0 + t * kBN;
     const int nk = min(kBN, k1 - key0);
     __syncthreads();                      // previous tile fully consumed
     store_tile<D>(sm, st, tid);
     __syncthreads();
-    if (key0 + kBN < k1) load_tile<D>(st, kp, vp, trow, key0 + kBN, min(kBN, k1 - key0 - kBN), slot_stride, tid);
+    if (t + 1 < ntiles) {
+      issue_tile<D>(st, kp, vp, s_next, slot_stride, tid, wave_u);
+      if (t + 2 < ntiles) s_next = tile_slots(trow, key0 + 2 * kBN, min(kBN, k1 - key0 - 2 * kBN), lane);
+    }
     if (has_rows) {
       if (nk == kBN && key0 + kBN <= mask_from) wave_tile<D, false>(ws, sm, qf, lane, nk, key0, lim, c);
       else wave_tile<D, true>(ws, sm, qf, lane, nk, key0, lim, c);
@@ -265,7 +283,7 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Tile<D>& sm, const
 
 // ------------------------------------------------------------------ extend (bf16)
 template <int D>
-__global__ void __launch_bounds__(kThreads) extend_bf16_kernel(
+__global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
@@ -297,7 +315,7 @@ __global__ void __launch_bounds__(kThreads) extend_bf16_kernel(
   const bool has_rows = wave * 32 < ntok * G;
   const float c = sm_scale * kLog2e;
   stream_keys<D>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
-                 int64_t(Hkv) * D, 0, key_end, mask_from, lim, c, has_rows, tid);
+                 uint32_t(Hkv * D), 0, key_end, mask_from, lim, c, has_rows, tid);
   if (!valid) return;
   float l = ws.l + __shfl_xor(ws.l, 32);
   float inv = l > 0.f ? 1.f / l : 0.f;
@@ -329,7 +347,6 @@ struct DecodeArgs {
   float sm_scale;
   float* o_part;              // [Hkv][P][G][D]
   float* lse_part;            // [Hkv][P][G]
-  int* cnt;                   // [B][Hkv]
   int64_t n_partials;
   uint16_t* out;              // [B][Hq][D]
   float* lse_out;             // [B][Hq] or nullptr
@@ -342,33 +359,28 @@ struct PartList {
   __device__ int at(int i) const { return list ? list[i] : base + i; }
 };
 
-template <int D>
-__device__ void merge_request(const DecodeArgs& a, int b, int kvh, const PartList& pl, int tid) {
-  const int G = a.Hq / a.Hkv;
-  const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
-  const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int g = e / D, d = e % D;
-    float mx = -INFINITY;
-    for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g]);
-    float wsum = 0.f, acc = 0.f;
-    for (int i = 0; i < pl.n; ++i) {
-      const int64_t p = pl.at(i);
-      const float w = __expf(lp[p * G + g] - mx);
-      wsum += w;
-      acc = fmaf(w, op[(p * G + g) * D + d], acc);
-    }
-    const int64_t orow = int64_t(b) * a.Hq + kvh * G + g;
-    a.out[orow * D + d] = f2bf(acc / wsum);
-    if (d == 0 && a.lse_out) a.lse_out[orow] = mx + __logf(wsum);
+// Partials of request b (plan: its CSR list; flat: its consecutive chunks).
+__device__ __forceinline__ PartList part_list(const DecodeArgs& a, int b) {
+  PartList pl;
+  if (a.plan) {
+    const int32_t* pp = a.plan + a.plan[7];
+    pl.list = a.plan + a.plan[8] + pp[b];
+    pl.base = 0;
+    pl.n = pp[b + 1] - pp[b];
+  } else {
+    pl.list = nullptr;
+    pl.base = b * a.flat_nch;
+    pl.n = (a.seq_lens[b] + rs::kFlatChunk - 1) / rs::kFlatChunk;
   }
+  return pl;
 }
 
+// One work item per (item, KV head): its key chunk for all query rows of its row tile.
+// A request covered by this single item gets its final output here; otherwise the
+// item writes one partial (o / l, lse) per (request, head) for decode_merge_kernel.
 template <int D>
-__global__ void __launch_bounds__(kThreads) decode_bf16_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) {
   __shared__ Tile<D> sm;
-  __shared__ int s_req[rs::kMaxRowsPerItem];
-  __shared__ int s_last[rs::kMaxRowsPerItem];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
   const int kvh = blockIdx.x % a.Hkv;
@@ -396,94 +408,66 @@ __global__ void __launch_bounds__(kThreads) decode_bf16_kernel(DecodeArgs a) {
   wave_init<D>(ws);
   const bool has_rows = wave * 32 < nreq * G;
   stream_keys<D>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
-                 a.req_to_token + int64_t(rep) * a.ld, int64_t(a.Hkv) * D, k0, k1, k1, INT32_MAX,
+                 a.req_to_token + int64_t(rep) * a.ld, uint32_t(a.Hkv * D), k0, k1, k1, INT32_MAX,
                  a.sm_scale * kLog2e, has_rows, tid);
-
-  // partial count of each request of this item
-  int npart = 0;
-  PartList pl{nullptr, 0, 0};
-  if (valid) {
-    if (a.plan) {
-      const int32_t* pp = a.plan + a.plan[7];
-      pl.list = a.plan + a.plan[8] + pp[b];
-      pl.n = pp[b + 1] - pp[b];
-    } else {
-      pl.base = b * a.flat_nch;
-      pl.n = (a.seq_lens[b] + rs::kFlatChunk - 1) / rs::kFlatChunk;
-    }
-    npart = pl.n;
-  }
+  if (!valid) return;
   const float l = ws.l + __shfl_xor(ws.l, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = ws.m * a.sm_scale + __logf(l);
   const int hi = lane >> 5;
-  if (valid) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (npart == 1) {                    // this item covers the request: final output
-      uint16_t* orow = a.out + qrow_idx * D;
+  if (part_list(a, b).n == 1) {          // this item covers the request: final output
+    uint16_t* orow = a.out + qrow_idx * D;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          int d = mb * 32 + 8 * q4 + 4 * hi;
-          uint2 u;
-          u.x = pack_bf16(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv);
-          u.y = pack_bf16(ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + d) = u;
-        }
-      if (hi == 0 && a.lse_out) a.lse_out[qrow_idx] = ws.m * a.sm_scale + __logf(l);
-    } else {
-      const int64_t p = part_base + j;
-      float* orow = a.o_part + ((int64_t(kvh) * a.n_partials + p) * G + g) * D;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          int d = mb * 32 + 8 * q4 + 4 * hi;
-          float4 v = make_float4(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv,
-                                 ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
-          *reinterpret_cast<float4*>(orow + d) = v;
-        }
-      if (hi == 0) a.lse_part[(int64_t(kvh) * a.n_partials + p) * G + g] = ws.m * a.sm_scale + __logf(l);
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = mb * 32 + 8 * q4 + 4 * hi;
+        uint2 u;
+        u.x = pack_bf16(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv);
+        u.y = pack_bf16(ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+    if (hi == 0 && a.lse_out) a.lse_out[qrow_idx] = lse;
+    return;
   }
-  // completion: the last item to finish a (request, KV head) merges its partials
-  __threadfence();
-  __syncthreads();
-  if (tid < nreq) {
-    const int bb = item_req ? item_req[tid] : rep;
-    int n;
-    if (a.plan) {
-      const int32_t* pp = a.plan + a.plan[7];
-      n = pp[bb + 1] - pp[bb];
-    } else {
-      n = (a.seq_lens[bb] + rs::kFlatChunk - 1) / rs::kFlatChunk;
+  const int64_t p = part_base + j;
+  float* orow = a.o_part + ((int64_t(kvh) * a.n_partials + p) * G + g) * D;
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = mb * 32 + 8 * q4 + 4 * hi;
+      *reinterpret_cast<float4*>(orow + d) =
+          make_float4(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv, ws.o[mb][4 * q4 + 2] * inv,
+                      ws.o[mb][4 * q4 + 3] * inv);
     }
-    int last = 0;
-    if (n > 1) {
-      int old = __hip_atomic_fetch_add(&a.cnt[int64_t(bb) * a.Hkv + kvh], 1, __ATOMIC_ACQ_REL,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-      last = (old == n - 1);
+  if (hi == 0) a.lse_part[(int64_t(kvh) * a.n_partials + p) * G + g] = lse;
+}
+
+// Log-sum-exp merge of each (request, KV head)'s partials:
+//   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
+template <int D>
+__global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const PartList pl = part_list(a, b);
+  if (pl.n <= 1) return;
+  const int G = a.Hq / a.Hkv;
+  const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
+  const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
+  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+    const int g = e / D, d = e % D;
+    float mx = -INFINITY;
+    for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g]);
+    float wsum = 0.f, acc = 0.f;
+    for (int i = 0; i < pl.n; ++i) {
+      const int64_t p = pl.at(i);
+      const float w = __expf(lp[p * G + g] - mx);
+      wsum += w;
+      acc = fmaf(w, op[(p * G + g) * D + d], acc);
     }
-    s_req[tid] = bb;
-    s_last[tid] = last;
-  }
-  __syncthreads();
-  for (int r = 0; r < nreq; ++r) {
-    if (!s_last[r]) continue;
-    __threadfence();
-    const int bb = s_req[r];
-    PartList q;
-    if (a.plan) {
-      const int32_t* pp = a.plan + a.plan[7];
-      q.list = a.plan + a.plan[8] + pp[bb];
-      q.base = 0;
-      q.n = pp[bb + 1] - pp[bb];
-    } else {
-      q.list = nullptr;
-      q.base = bb * a.flat_nch;
-      q.n = (a.seq_lens[bb] + rs::kFlatChunk - 1) / rs::kFlatChunk;
-    }
-    merge_request<D>(a, bb, kvh, q, tid);
-    if (tid == 0) a.cnt[int64_t(bb) * a.Hkv + kvh] = 0;     // ready for the next launch
+    const int64_t orow = int64_t(b) * a.Hq + kvh * G + g;
+    a.out[orow * D + d] = f2bf(acc / wsum);
+    if (d == 0 && a.lse_out) a.lse_out[orow] = mx + __logf(wsum);
   }
 }
 
@@ -741,12 +725,17 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
   char* w = static_cast<char*>(ws);
   a.o_part = reinterpret_cast<float*>(w + wl.o_off);
   a.lse_part = reinterpret_cast<float*>(w + wl.lse_off);
-  a.cnt = reinterpret_cast<int*>(w + wl.cnt_off);
   a.n_partials = P;
   a.out = static_cast<uint16_t*>(out);
   a.lse_out = lse_out;
-  if (D == 128) hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(unsigned(items * Hkv)), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(unsigned(items * Hkv)), dim3(kThreads), 0, s, a);
+  const dim3 g_items(unsigned(items * Hkv)), g_merge(unsigned(int64_t(B) * Hkv));
+  if (D == 128) {
+    hipLaunchKernelGGL(decode_bf16_kernel<128>, g_items, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, g_merge, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(decode_bf16_kernel<64>, g_items, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, g_merge, dim3(kThreads), 0, s, a);
+  }
   return hip_check("rs_decode_attention");
 }
 

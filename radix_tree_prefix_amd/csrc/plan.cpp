@@ -49,8 +49,8 @@ WsLayout ws_layout(int64_t n_partials, int32_t B, int32_t Hq, int32_t Hkv, int32
   int32_t G = Hq / Hkv;
   w.o_off = 0;
   w.lse_off = align256(w.o_off + int64_t(Hkv) * n_partials * G * D * 4);
-  w.cnt_off = align256(w.lse_off + int64_t(Hkv) * n_partials * G * 4);
-  w.bytes = align256(w.cnt_off + int64_t(B) * Hkv * 4);
+  w.bytes = align256(w.lse_off + int64_t(Hkv) * n_partials * G * 4);
+  (void)B;
   return w;
 }
 

@@ -16,10 +16,10 @@ constexpr int64_t kDecodeItemsTarget = 2048; // items x KV heads the chunk size 
 constexpr int64_t kMinChunk = 64;
 constexpr int64_t kMaxChunk = 8192;
 
-// Decode workspace: o partials float [Hkv][P][G][D], lse partials float [Hkv][P][G],
-// completion counters int32 [B][Hkv]; each region 256-byte aligned.
+// Decode workspace: o partials float [Hkv][P][G][D], lse partials float [Hkv][P][G];
+// each region 256-byte aligned.
 struct WsLayout {
-  int64_t o_off, lse_off, cnt_off, bytes;
+  int64_t o_off, lse_off, bytes;
 };
 WsLayout ws_layout(int64_t n_partials, int32_t B, int32_t Hq, int32_t Hkv, int32_t D);
 const rs_plan_info_t* plan_info(const rs_plan* p);
