@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel runs of the other configs")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path has no cross-GPU step); "
@@ -291,6 +293,15 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "no GPU visible"
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
     print(f"[bench] setup config {args.config}", file=sys.stderr, flush=True)
     st = setup(args.config)
     print(f"[bench] setup done in {st.host_s:.1f}s (history {st.history_s:.2f}s, admit {st.admit_s:.3f}s)",

@@ -40,8 +40,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kBN = 64;       // keys per LDS tile
-constexpr int kKPad = 8;      // bf16 padding per K row in LDS
-constexpr int kVPad = 8;      // bf16 padding per V^T row in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
@@ -53,29 +51,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
-template <int D>
-struct __align__(16) Tile {
-  uint16_t k[kBN][D + kKPad];
-  uint16_t vt[D][kBN + kVPad];
-};
+// One stage of a K/V tile in LDS, stored as 16-byte chunk-columns: chunk c (elements
+// 8c..8c+7) of key t sits at byte c*kColBytes + 16*t.  A column holds one chunk of all kBN
+// keys plus 64 bytes of padding, which puts neighbouring columns 16 banks apart.  The
+// rows arrive straight from global memory (global_load_lds_dwordx4: lane t of a wave
+// fetches chunk c of key t into column c), so there are no staging registers and no LDS
+// write instructions, and every operand read below is one base register plus constants.
+constexpr int kColBytes = kBN * 16 + 64;
 
-// ------------------------------------------------------------------ tile loads
-// Per-thread staging registers for one K/V tile.
 template <int D>
-struct Stage {
-  static constexpr int kChunksPerRow = D / 8;                          // 16-byte chunks
-  static constexpr int kK = kBN * kChunksPerRow / kThreads;            // K chunks per thread
-  static constexpr int kLanesPerRow = D / 2;                           // dwords per V row
-  static constexpr int kRowsPerWaveLoad = 64 / kLanesPerRow;           // 1 (D=128) or 2 (D=64)
-  static constexpr int kVBlocks = 8 / (4 * kRowsPerWaveLoad);          // 8-key blocks per thread
-  uint4 k[kK];
-  uint32_t v[kVBlocks][8];
+struct __align__(16) Stage {
+  char k[(D / 8) * kColBytes];
+  char v[(D / 8) * kColBytes];
 };
-
-// Keys of the 8-key block kb (0..7) in the permuted V^T order: LDS positions kb*8+i hold
-// key 16*(kb/2) + 8*(i/4) + 4*(kb%2) + i%4.  That order makes P^T's rows (straight from
-// the S^T accumulator) and V^T's columns pair up in the PV MFMA.
-__device__ __forceinline__ int vkey(int kb, int i) { return 16 * (kb >> 1) + 8 * (i >> 2) + 4 * (kb & 1) + (i & 3); }
 
 // Slot ids of one tile: lane l of every wave holds the slot of key key0 + min(l, nk-1).
 // Keys past nk repeat the last valid slot (an in-bounds row); they are masked later.
@@ -83,65 +71,21 @@ __device__ __forceinline__ int tile_slots(const int32_t* __restrict__ trow, int 
   return trow[key0 + min(lane, nk - 1)];
 }
 
-// Issue the global loads of one tile into the staging registers.  `sreg` is the tile's
-// slot register (tile_slots).  K: 16-byte chunks, the row's slot fetched from the lane
-// that holds it; V: one whole KV-head row per wave instruction (wave-uniform slot), so
-// the address is a scalar base plus the lane's dword offset.
-template <int D>
-__device__ __forceinline__ void issue_tile(Stage<D>& st, const uint16_t* __restrict__ kp,
-                                           const uint16_t* __restrict__ vp, int sreg, uint32_t slot_stride,
-                                           int tid, int wave_u) {
-  using S = Stage<D>;
-#pragma unroll
-  for (int i = 0; i < S::kK; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
-    const uint32_t slot = uint32_t(__shfl(sreg, row));
-    st.k[i] = *reinterpret_cast<const uint4*>(kp + uint64_t(slot) * slot_stride + ch * 8);
-  }
-  const int lane = tid & 63;
-  const int sub = lane / S::kLanesPerRow, dw = lane % S::kLanesPerRow;
-#pragma unroll
-  for (int blk = 0; blk < S::kVBlocks; ++blk) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t slot;
-      if constexpr (S::kRowsPerWaveLoad == 1) {
-        slot = uint32_t(__builtin_amdgcn_readlane(sreg, vkey(blk * 4 + wave_u, i)));
-      } else {
-        slot = uint32_t(__shfl(sreg, vkey((blk * 4 + wave_u) * S::kRowsPerWaveLoad + sub, i)));
-      }
-      st.v[blk][i] = *reinterpret_cast<const uint32_t*>(vp + uint64_t(slot) * slot_stride + 2 * dw);
-    }
-  }
-}
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Issue the global->LDS loads of one tile: wave w fills chunk-columns
+// [w*D/32, (w+1)*D/32) of K and of V; sreg = tile_slots (this lane's key's slot).
 template <int D>
-__device__ __forceinline__ void store_tile(Tile<D>& sm, const Stage<D>& st, int tid) {
-  using S = Stage<D>;
+__device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* __restrict__ kp,
+                                           const uint16_t* __restrict__ vp, int sreg, uint32_t slot_stride,
+                                           int wave_u) {
+  constexpr int CPW = D / 32;                         // columns per wave
+  const uint64_t row = uint64_t(uint32_t(sreg)) * slot_stride;
 #pragma unroll
-  for (int i = 0; i < S::kK; ++i) {
-    int c = tid + i * kThreads;
-    int row = c / S::kChunksPerRow, ch = c % S::kChunksPerRow;
-    *reinterpret_cast<uint4*>(&sm.k[row][ch * 8]) = st.k[i];
-  }
-  const int wave = tid >> 6, lane = tid & 63;
-  const int sub = lane / S::kLanesPerRow, dw = lane % S::kLanesPerRow;
-#pragma unroll
-  for (int blk = 0; blk < S::kVBlocks; ++blk) {
-    int kb = (blk * 4 + wave) * S::kRowsPerWaveLoad + sub;
-    const uint32_t* v = st.v[blk];
-    uint4 lo, hi;   // d = 2*dw (low halves) and d = 2*dw+1 (high halves) for the 8 keys
-    lo.x = (v[0] & 0xffffu) | (v[1] << 16);
-    lo.y = (v[2] & 0xffffu) | (v[3] << 16);
-    lo.z = (v[4] & 0xffffu) | (v[5] << 16);
-    lo.w = (v[6] & 0xffffu) | (v[7] << 16);
-    hi.x = (v[0] >> 16) | (v[1] & 0xffff0000u);
-    hi.y = (v[2] >> 16) | (v[3] & 0xffff0000u);
-    hi.z = (v[4] >> 16) | (v[5] & 0xffff0000u);
-    hi.w = (v[6] >> 16) | (v[7] & 0xffff0000u);
-    *reinterpret_cast<uint4*>(&sm.vt[2 * dw][kb * 8]) = lo;
-    *reinterpret_cast<uint4*>(&sm.vt[2 * dw + 1][kb * 8]) = hi;
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave_u * CPW + i;
+    __builtin_amdgcn_global_load_lds(kp + row + c * 8, (lds_ptr)(dst.k + c * kColBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + row + c * 8, (lds_ptr)(dst.v + c * kColBytes), 16, 0, 0);
   }
 }
 
@@ -175,37 +119,40 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t* __r
   }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 // One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
 // visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
 template <int D, bool MASK>
-__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Tile<D>& sm, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
                                           int lane, int nk, int key_pos0, int lim, float c) {
   const int r32 = lane & 31, hi = lane >> 5;
+  const char* kb = sm.k + hi * kColBytes + r32 * 16;     // chunk 2ks+hi of key r32
   f32x16 s[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb32 = 0; kb32 < 2; ++kb32) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+    for (int j = 0; j < 16; ++j) s[kb32][j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[kb * 32 + r32][16 * ks + 8 * hi]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 2 * ks * kColBytes + kb32 * 32 * 16);
+      s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb32], 0, 0, 0);
     }
   }
   if (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        int t = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-        if (t >= nk || key_pos0 + t > lim) s[kb][j] = -INFINITY;
+        const int t = kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        if (t >= nk || key_pos0 + t > lim) s[kb32][j] = -INFINITY;
       }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb32][j]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(ws.m, mx);
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -213,11 +160,11 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Tile<D>& sm, c
   const float mc = m_use * c;
   float sum = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float p = exp2f(fmaf(s[kb][j], c, -mc));
-      s[kb][j] = p;
+      const float p = exp2f(fmaf(s[kb32][j], c, -mc));
+      s[kb32][j] = p;
       sum += p;
     }
   ws.l = fmaf(ws.l, alpha, sum);
@@ -226,30 +173,40 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Tile<D>& sm, c
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) ws.o[mb][j] *= alpha;
+  // V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
+  // element i%4 of the 8-byte pieces read by lanes i/4 + 4k (k = 0..3).  Provider lane j
+  // reads key kbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
+  // V[kbase + k][dbase + i], k = 0..3: the four keys of its P^T slots 4r..4r+3.
+  const int i16 = lane & 15, gpar = (lane >> 4) & 1;
+  const char* vb = sm.v + (2 * gpar + ((i16 & 3) >> 1)) * kColBytes + (hi * 4 + (i16 >> 2)) * 16 + (i16 & 1) * 8;
 #pragma unroll
   for (int kstep = 0; kstep < 4; ++kstep) {
-    const int kb = kstep >> 1, h8 = (kstep & 1) * 8;
+    const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
     uint4 pu;
-    pu.x = pack_bf16(s[kb][h8 + 0], s[kb][h8 + 1]);
-    pu.y = pack_bf16(s[kb][h8 + 2], s[kb][h8 + 3]);
-    pu.z = pack_bf16(s[kb][h8 + 4], s[kb][h8 + 5]);
-    pu.w = pack_bf16(s[kb][h8 + 6], s[kb][h8 + 7]);
-    bf16x8 b = __builtin_bit_cast(bf16x8, pu);
+    pu.x = pack_bf16(s[kb32][h8 + 0], s[kb32][h8 + 1]);
+    pu.y = pack_bf16(s[kb32][h8 + 2], s[kb32][h8 + 3]);
+    pu.z = pack_bf16(s[kb32][h8 + 4], s[kb32][h8 + 5]);
+    pu.w = pack_bf16(s[kb32][h8 + 6], s[kb32][h8 + 7]);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, pu);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[mb * 32 + r32][16 * kstep + 8 * hi]);
+      const char* p0 = vb + mb * 4 * kColBytes + kstep * 16 * 16;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * 16));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+          lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
       ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
     }
   }
 }
 
 // Stream keys [k0, k1) of one index-table row through the workgroup.  Waves with
-// has_rows run the math; every wave helps load.  mask_from: first key position at
+// has_rows run the math; every wave issues loads.  mask_from: first key position at
 // which any row of the workgroup may need masking (keys >= k1 are always masked).
-// Pipeline: while tile t is computed from LDS, tile t+1's K/V loads and tile t+2's
-// slot ids are in flight.
+// Two LDS stages: while tile t is computed, tile t+1 is landing in the other stage and
+// tile t+2's slot ids are in flight.
 template <int D>
-__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Tile<D>& sm, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                                             const int32_t* __restrict__ trow, uint32_t slot_stride, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
@@ -257,26 +214,24 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Tile<D>& sm, const
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntiles = (k1 - k0 + kBN - 1) / kBN;
-  Stage<D> st;
   int s_next = 0;
   {
     const int s0 = tile_slots(trow, k0, min(kBN, k1 - k0), lane);
+    issue_tile<D>(sm[0], kp, vp, s0, slot_stride, wave_u);
     if (ntiles > 1) s_next = tile_slots(trow, k0 + kBN, min(kBN, k1 - k0 - kBN), lane);
-    issue_tile<D>(st, kp, vp, s0, slot_stride, tid, wave_u);
   }
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = k0 + t * kBN;
     const int nk = min(kBN, k1 - key0);
-    __syncthreads();                      // previous tile fully consumed
-    store_tile<D>(sm, st, tid);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");   // this wave's loads of tile t have landed
+    __syncthreads();                                      // ... and every wave's; stage (t+1)%2 is free
     if (t + 1 < ntiles) {
-      issue_tile<D>(st, kp, vp, s_next, slot_stride, tid, wave_u);
+      issue_tile<D>(sm[(t + 1) & 1], kp, vp, s_next, slot_stride, wave_u);
       if (t + 2 < ntiles) s_next = tile_slots(trow, key0 + 2 * kBN, min(kBN, k1 - key0 - 2 * kBN), lane);
     }
     if (has_rows) {
-      if (nk == kBN && key0 + kBN <= mask_from) wave_tile<D, false>(ws, sm, qf, lane, nk, key0, lim, c);
-      else wave_tile<D, true>(ws, sm, qf, lane, nk, key0, lim, c);
+      if (nk == kBN && key0 + kBN <= mask_from) wave_tile<D, false>(ws, sm[t & 1], qf, lane, nk, key0, lim, c);
+      else wave_tile<D, true>(ws, sm[t & 1], qf, lane, nk, key0, lim, c);
     }
   }
 }
@@ -288,7 +243,7 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
     int Hkv, float sm_scale, uint16_t* __restrict__ out) {
-  __shared__ Tile<D> sm;
+  __shared__ Stage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
   const int tpb = 128 / G;                        // tokens per tile
@@ -380,7 +335,7 @@ __device__ __forceinline__ PartList part_list(const DecodeArgs& a, int b) {
 // item writes one partial (o / l, lse) per (request, head) for decode_merge_kernel.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) {
-  __shared__ Tile<D> sm;
+  __shared__ Stage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
   const int kvh = blockIdx.x % a.Hkv;
