@@ -123,9 +123,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
 // visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
-template <int D, bool MASK>
+template <int D>
 __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
-                                          int lane, int nk, int key_pos0, int lim, float c) {
+                                          int lane, bool mask, int nk, int key_pos0, int lim, float c) {
   const int r32 = lane & 31, hi = lane >> 5;
   const char* kb = sm.k + hi * kColBytes + r32 * 16;     // chunk 2ks+hi of key r32
   f32x16 s[2];
@@ -139,7 +139,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
       s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb32], 0, 0, 0);
     }
   }
-  if (MASK) {
+  if (mask) {                             // wave-uniform: only the ragged or diagonal tiles
 #pragma unroll
     for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
@@ -156,14 +156,15 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(ws.m, mx);
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f((ws.m - m_use) * c);
+  // v_exp_f32 directly: results below 2^-126 flush to zero, which softmax weights can afford
+  const float alpha = __builtin_amdgcn_exp2f((ws.m - m_use) * c);
   const float mc = m_use * c;
   float sum = 0.f;
 #pragma unroll
   for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float p = exp2f(fmaf(s[kb32][j], c, -mc));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
       s[kb32][j] = p;
       sum += p;
     }
@@ -205,7 +206,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
 // which any row of the workgroup may need masking (keys >= k1 are always masked).
 // Two LDS stages: while tile t is computed, tile t+1 is landing in the other stage and
 // tile t+2's slot ids are in flight.
-template <int D>
+template <int D, bool SKIP_EMPTY>
 __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                                             const int32_t* __restrict__ trow, uint32_t slot_stride, int k0, int k1,
@@ -223,15 +224,19 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2],
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = k0 + t * kBN;
     const int nk = min(kBN, k1 - key0);
-    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");   // this wave's loads of tile t have landed
-    __syncthreads();                                      // ... and every wave's; stage (t+1)%2 is free
+    // This wave's loads of tile t have landed (the next tile's slot ids went out with them,
+    // so waiting for every load costs nothing extra); after the barrier every wave's have,
+    // and every wave is done reading stage (t+1)%2.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (t + 1 < ntiles) {
       issue_tile<D>(sm[(t + 1) & 1], kp, vp, s_next, slot_stride, wave_u);
       if (t + 2 < ntiles) s_next = tile_slots(trow, key0 + 2 * kBN, min(kBN, k1 - key0 - 2 * kBN), lane);
     }
-    if (has_rows) {
-      if (nk == kBN && key0 + kBN <= mask_from) wave_tile<D, false>(ws, sm[t & 1], qf, lane, nk, key0, lim, c);
-      else wave_tile<D, true>(ws, sm[t & 1], qf, lane, nk, key0, lim, c);
+    // Extend computes on every wave (a wave past the last token has only masked rows,
+    // which contribute exact zeros); decode skips waves without rows (SKIP_EMPTY).
+    if (!SKIP_EMPTY || has_rows) {
+      const bool mask = nk < kBN || key0 + kBN > mask_from;
+      wave_tile<D>(ws, sm[t & 1], qf, lane, mask, nk, key0, lim, c);
     }
   }
 }
@@ -269,7 +274,7 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
   const int mask_from = prefix + t0 + 1;          // keys below this are visible to every row
   const bool has_rows = wave * 32 < ntok * G;
   const float c = sm_scale * kLog2e;
-  stream_keys<D>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
+  stream_keys<D, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
                  uint32_t(Hkv * D), 0, key_end, mask_from, lim, c, has_rows, tid);
   if (!valid) return;
   float l = ws.l + __shfl_xor(ws.l, 32);
@@ -362,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   WaveState<D> ws;
   wave_init<D>(ws);
   const bool has_rows = wave * 32 < nreq * G;
-  stream_keys<D>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
+  stream_keys<D, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
                  a.req_to_token + int64_t(rep) * a.ld, uint32_t(a.Hkv * D), k0, k1, k1, INT32_MAX,
                  a.sm_scale * kLog2e, has_rows, tid);
   if (!valid) return;
