@@ -51,18 +51,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
-// One stage of a K/V tile in LDS, stored as 16-byte chunk-columns: chunk c (elements
-// 8c..8c+7) of key t sits at byte c*kColBytes + 16*t.  A column holds one chunk of all kBN
-// keys plus 64 bytes of padding, which puts neighbouring columns 16 banks apart.  The
-// rows arrive straight from global memory (global_load_lds_dwordx4: lane t of a wave
-// fetches chunk c of key t into column c), so there are no staging registers and no LDS
-// write instructions, and every operand read below is one base register plus constants.
-constexpr int kColBytes = kBN * 16 + 64;
+// One stage of a K/V tile in LDS: kBN key rows of K and of V, row-major, rows padded
+// (K: +16 bytes, V: +32 bytes) so that the MFMA operand reads below hit distinct banks.
+// Rows arrive straight from global memory: one global_load_lds_dword per row, the 64
+// lanes of a wave covering the row's Hkv-slice (256 bytes at d=128) -- a fully
+// coalesced request with a wave-uniform slot -- and no staging registers or LDS writes.
+template <int D>
+struct StageLayout {
+  static constexpr int kK = D * 2 + 16;       // K row stride (bytes)
+  static constexpr int kV = D * 2 + 32;       // V row stride (bytes)
+};
 
 template <int D>
 struct __align__(16) Stage {
-  char k[(D / 8) * kColBytes];
-  char v[(D / 8) * kColBytes];
+  char k[kBN * StageLayout<D>::kK];
+  char v[kBN * StageLayout<D>::kV];
 };
 
 // Slot ids of one tile: lane l of every wave holds the slot of key key0 + min(l, nk-1).
@@ -73,19 +76,22 @@ __device__ __forceinline__ int tile_slots(const int32_t* __restrict__ trow, int 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Issue the global->LDS loads of one tile: wave w fills chunk-columns
-// [w*D/32, (w+1)*D/32) of K and of V; sreg = tile_slots (this lane's key's slot).
+// Issue the global->LDS loads of one tile: wave w fills key rows [w*kBN/4, (w+1)*kBN/4)
+// of K and of V; sreg = tile_slots (lane t holds key t's slot).
 template <int D>
 __device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* __restrict__ kp,
                                            const uint16_t* __restrict__ vp, int sreg, uint32_t slot_stride,
-                                           int wave_u) {
-  constexpr int CPW = D / 32;                         // columns per wave
-  const uint64_t row = uint64_t(uint32_t(sreg)) * slot_stride;
+                                           int lane, int wave_u) {
+  constexpr int RPW = kBN / 4;                        // rows per wave
+  using L = StageLayout<D>;
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int c = wave_u * CPW + i;
-    __builtin_amdgcn_global_load_lds(kp + row + c * 8, (lds_ptr)(dst.k + c * kColBytes), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + row + c * 8, (lds_ptr)(dst.v + c * kColBytes), 16, 0, 0);
+  for (int i = 0; i < RPW; ++i) {
+    const int r = wave_u * RPW + i;
+    const uint64_t row = uint64_t(uint32_t(__builtin_amdgcn_readlane(sreg, r))) * slot_stride;
+    if (D == 128 || lane < D / 2) {
+      __builtin_amdgcn_global_load_lds(kp + row + 2 * lane, (lds_ptr)(dst.k + r * L::kK), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + row + 2 * lane, (lds_ptr)(dst.v + r * L::kV), 4, 0, 0);
+    }
   }
 }
 
@@ -126,8 +132,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
                                           int lane, bool mask, int nk, int key_pos0, int lim, float c) {
+  using L = StageLayout<D>;
   const int r32 = lane & 31, hi = lane >> 5;
-  const char* kb = sm.k + hi * kColBytes + r32 * 16;     // chunk 2ks+hi of key r32
+  const char* kb = sm.k + r32 * L::kK + hi * 16;         // key r32, elements 16ks + 8hi ..
   f32x16 s[2];
 #pragma unroll
   for (int kb32 = 0; kb32 < 2; ++kb32) {
@@ -135,7 +142,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     for (int j = 0; j < 16; ++j) s[kb32][j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 2 * ks * kColBytes + kb32 * 32 * 16);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + kb32 * 32 * L::kK + ks * 32);
       s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb32], 0, 0, 0);
     }
   }
@@ -179,7 +186,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   // reads key kbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
   // V[kbase + k][dbase + i], k = 0..3: the four keys of its P^T slots 4r..4r+3.
   const int i16 = lane & 15, gpar = (lane >> 4) & 1;
-  const char* vb = sm.v + (2 * gpar + ((i16 & 3) >> 1)) * kColBytes + (hi * 4 + (i16 >> 2)) * 16 + (i16 & 1) * 8;
+  const char* vb = sm.v + (hi * 4 + (i16 >> 2)) * L::kV + (16 * gpar + 4 * (i16 & 3)) * 2;
 #pragma unroll
   for (int kstep = 0; kstep < 4; ++kstep) {
     const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
@@ -191,9 +198,9 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     const bf16x8 b = __builtin_bit_cast(bf16x8, pu);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      const char* p0 = vb + mb * 4 * kColBytes + kstep * 16 * 16;
+      const char* p0 = vb + kstep * 16 * L::kV + mb * 64;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * 16));
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * L::kV));
       const bf16x8 a = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
           lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
       ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
@@ -218,7 +225,7 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2],
   int s_next = 0;
   {
     const int s0 = tile_slots(trow, k0, min(kBN, k1 - k0), lane);
-    issue_tile<D>(sm[0], kp, vp, s0, slot_stride, wave_u);
+    issue_tile<D>(sm[0], kp, vp, s0, slot_stride, lane, wave_u);
     if (ntiles > 1) s_next = tile_slots(trow, k0 + kBN, min(kBN, k1 - k0 - kBN), lane);
   }
   for (int t = 0; t < ntiles; ++t) {
@@ -229,7 +236,7 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2],
     // and every wave is done reading stage (t+1)%2.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (t + 1 < ntiles) {
-      issue_tile<D>(sm[(t + 1) & 1], kp, vp, s_next, slot_stride, wave_u);
+      issue_tile<D>(sm[(t + 1) & 1], kp, vp, s_next, slot_stride, lane, wave_u);
       if (t + 2 < ntiles) s_next = tile_slots(trow, key0 + 2 * kBN, min(kBN, k1 - key0 - 2 * kBN), lane);
     }
     // Extend computes on every wave (a wave past the last token has only masked rows,
