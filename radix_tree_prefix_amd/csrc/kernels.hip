@@ -68,12 +68,6 @@ struct __align__(16) Stage {
   char v[kBN * StageLayout<D>::kV];
 };
 
-// Slot ids of one tile: lane l of every wave holds the slot of key key0 + min(l, nk-1).
-// Keys past nk repeat the last valid slot (an in-bounds row); they are masked later.
-__device__ __forceinline__ int tile_slots(const int32_t* __restrict__ trow, int key0, int nk, int lane) {
-  return trow[key0 + min(lane, nk - 1)];
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Issue the global->LDS loads of one tile: wave w fills key rows [w*kBN/4, (w+1)*kBN/4)
@@ -208,42 +202,60 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   }
 }
 
-// Stream keys [k0, k1) of one index-table row through the workgroup.  Waves with
-// has_rows run the math; every wave issues loads.  mask_from: first key position at
-// which any row of the workgroup may need masking (keys >= k1 are always masked).
-// Two LDS stages: while tile t is computed, tile t+1 is landing in the other stage and
-// tile t+2's slot ids are in flight.
-template <int D, bool SKIP_EMPTY>
-__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[2], const bf16x8 (&qf)[D / 16],
+// Slot ids of one tile, clamped: lane l holds the slot of key min(key0 + l, k1 - 1).
+// Keys past the range repeat the last valid slot (an in-bounds row); they are masked.
+__device__ __forceinline__ int clamped_slots(const int32_t* __restrict__ trow, int key0, int k1, int lane) {
+  return trow[min(key0 + lane, k1 - 1)];
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Stream keys [k0, k1) of one index-table row through the workgroup, NS LDS stages deep.
+// Waves with has_rows run the math (SKIP_EMPTY) or every wave does (a wave past the last
+// token then has only masked rows, which contribute exact zeros); every wave issues loads.
+// Keys below mask_from are visible to every row; tiles reaching past it (and a ragged
+// last tile) take the masked path.
+//
+// Pipeline: at the top of iteration t the workgroup waits for tile t (this wave's loads,
+// then a barrier for everyone's, after which every wave is also done with the stage tile
+// t-1 used); it then issues the slot ids of tile t+NS and the loads of tile t+NS-1 into
+// that stage, and computes tile t.  While tile t+1 is in flight the wait leaves exactly
+// the loads issued after tile t's (one iteration's worth) outstanding.
+template <int D, int NS, bool SKIP_EMPTY>
+__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                                             const int32_t* __restrict__ trow, uint32_t slot_stride, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
   if (k0 >= k1) return;
+  constexpr int kDmaPerTile = 2 * (kBN / 4);          // K + V rows one wave issues per tile
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntiles = (k1 - k0 + kBN - 1) / kBN;
-  int s_next = 0;
-  {
-    const int s0 = tile_slots(trow, k0, min(kBN, k1 - k0), lane);
-    issue_tile<D>(sm[0], kp, vp, s0, slot_stride, lane, wave_u);
-    if (ntiles > 1) s_next = tile_slots(trow, k0 + kBN, min(kBN, k1 - k0 - kBN), lane);
-  }
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < ntiles) issue_tile<D>(sm[j], kp, vp, clamped_slots(trow, k0 + j * kBN, k1, lane), slot_stride, lane, wave_u);
+  int s_next = clamped_slots(trow, k0 + (NS - 1) * kBN, k1, lane);
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = k0 + t * kBN;
     const int nk = min(kBN, k1 - key0);
-    // This wave's loads of tile t have landed (the next tile's slot ids went out with them,
-    // so waiting for every load costs nothing extra); after the barrier every wave's have,
-    // and every wave is done reading stage (t+1)%2.
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t + 1 < ntiles) {
-      issue_tile<D>(sm[(t + 1) & 1], kp, vp, s_next, slot_stride, lane, wave_u);
-      if (t + 2 < ntiles) s_next = tile_slots(trow, key0 + 2 * kBN, min(kBN, k1 - key0 - 2 * kBN), lane);
+    // After tile t's loads came, in order: the next tiles' (issued one iteration each,
+    // kDmaPerTile + 1 instructions per iteration) -- exactly when all of them exist.
+    // (vmcnt counts to 63: a smaller count only waits a little longer)
+    constexpr int kAfter = (NS - 2) * (kDmaPerTile + 1) < 63 ? (NS - 2) * (kDmaPerTile + 1) : 63;
+    if (NS > 2 && t + NS - 2 < ntiles && t >= NS - 2) wait_vmcnt_barrier<kAfter>();
+    else wait_vmcnt_barrier<0>();
+    if (t + NS - 1 < ntiles) {
+      const int s_after = clamped_slots(trow, k0 + (t + NS) * kBN, k1, lane);
+      issue_tile<D>(sm[(t + NS - 1) % NS], kp, vp, s_next, slot_stride, lane, wave_u);
+      s_next = s_after;
     }
-    // Extend computes on every wave (a wave past the last token has only masked rows,
-    // which contribute exact zeros); decode skips waves without rows (SKIP_EMPTY).
     if (!SKIP_EMPTY || has_rows) {
       const bool mask = nk < kBN || key0 + kBN > mask_from;
-      wave_tile<D>(ws, sm[t & 1], qf, lane, mask, nk, key0, lim, c);
+      wave_tile<D>(ws, sm[t % NS], qf, lane, mask, nk, key0, lim, c);
     }
   }
 }
@@ -281,7 +293,7 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
   const int mask_from = prefix + t0 + 1;          // keys below this are visible to every row
   const bool has_rows = wave * 32 < ntok * G;
   const float c = sm_scale * kLog2e;
-  stream_keys<D, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
+  stream_keys<D, 2, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
                  uint32_t(Hkv * D), 0, key_end, mask_from, lim, c, has_rows, tid);
   if (!valid) return;
   float l = ws.l + __shfl_xor(ws.l, 32);
@@ -374,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   WaveState<D> ws;
   wave_init<D>(ws);
   const bool has_rows = wave * 32 < nreq * G;
-  stream_keys<D, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
+  stream_keys<D, 2, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
                  a.req_to_token + int64_t(rep) * a.ld, uint32_t(a.Hkv * D), k0, k1, k1, INT32_MAX,
                  a.sm_scale * kLog2e, has_rows, tid);
   if (!valid) return;
@@ -413,28 +425,69 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
 
 // Log-sum-exp merge of each (request, KV head)'s partials:
 //   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
+// The weights of up to kMergeBatch partials per head are computed once into LDS; then each
+// thread accumulates its output elements with independent, coalesced partial loads.
+constexpr int kMergeBatch = 64;
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
+  __shared__ float s_w[16 * kMergeBatch];            // weights [g][i], 16 heads per pass
+  __shared__ int s_p[kMergeBatch];
+  __shared__ float s_m[16], s_sum[16];
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const PartList pl = part_list(a, b);
   if (pl.n <= 1) return;
   const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x;
   const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
   const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
-  for (int e = threadIdx.x; e < G * D; e += kThreads) {
-    const int g = e / D, d = e % D;
-    float mx = -INFINITY;
-    for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g]);
-    float wsum = 0.f, acc = 0.f;
-    for (int i = 0; i < pl.n; ++i) {
-      const int64_t p = pl.at(i);
-      const float w = __expf(lp[p * G + g] - mx);
-      wsum += w;
-      acc = fmaf(w, op[(p * G + g) * D + d], acc);
+  for (int g0 = 0; g0 < G; g0 += 16) {                 // groups of up to 16 query heads
+    const int ng = min(16, G - g0);
+    // pass 1: running max and sum over all partials, per head
+    if (tid < ng) {
+      float mx = -INFINITY;
+      for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g0 + tid]);
+      float sum = 0.f;
+      for (int i = 0; i < pl.n; ++i) sum += __expf(lp[int64_t(pl.at(i)) * G + g0 + tid] - mx);
+      s_m[tid] = mx;
+      s_sum[tid] = sum;
     }
-    const int64_t orow = int64_t(b) * a.Hq + kvh * G + g;
-    a.out[orow * D + d] = f2bf(acc / wsum);
-    if (d == 0 && a.lse_out) a.lse_out[orow] = mx + __logf(wsum);
+    __syncthreads();
+    constexpr int kPer = 16 * D / kThreads;             // elements per thread (8 at d128)
+    float acc[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+    for (int i0 = 0; i0 < pl.n; i0 += kMergeBatch) {
+      const int nb = min(kMergeBatch, pl.n - i0);
+      if (tid < nb) s_p[tid] = pl.at(i0 + tid);
+      __syncthreads();
+      for (int x = tid; x < nb * ng; x += kThreads) {
+        const int i = x / ng, g = x % ng;
+        s_w[g * kMergeBatch + i] = __expf(lp[int64_t(s_p[i]) * G + g0 + g] - s_m[g]) / s_sum[g];
+      }
+      __syncthreads();
+      for (int i = 0; i < nb; ++i) {
+        const float* src = op + (int64_t(s_p[i]) * G + g0) * D;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int idx = tid + e * kThreads;            // (g, d) flattened, g < 16
+          const int g = idx / D;
+          if (g < ng) acc[e] = fmaf(s_w[g * kMergeBatch + i], src[idx], acc[e]);
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int idx = tid + e * kThreads;
+      const int g = idx / D, d = idx % D;
+      if (g < ng) {
+        const int64_t orow = int64_t(b) * a.Hq + kvh * G + g0 + g;
+        a.out[orow * D + d] = f2bf(acc[e]);
+        if (d == 0 && a.lse_out) a.lse_out[orow] = s_m[g] + __logf(s_sum[g]);
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -13,7 +13,7 @@ constexpr int32_t kItemWords = 8;            // k0, k1, rep_row, n_req, req_off,
 constexpr int32_t kMaxRowsPerItem = 128;     // 4 waves x 32 query rows
 constexpr int32_t kFlatChunk = 256;          // keys per item in the flat (plan-less) mode
 constexpr int64_t kDecodeItemsTarget = 2048; // items x KV heads the chunk size aims for
-constexpr int64_t kMinChunk = 64;
+constexpr int64_t kMinChunk = 512;           // >= 8 tiles per item: a work item pays several round trips before it streams
 constexpr int64_t kMaxChunk = 8192;
 
 // Decode workspace: o partials float [Hkv][P][G][D], lse partials float [Hkv][P][G];
