@@ -135,6 +135,7 @@ def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
         st.qo_indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(device)
         st.prefix_lens = torch.from_numpy(np.array([r.cached for r in ext], np.int32)).to(device)
         st.extend_lens = torch.from_numpy(lens).to(device)
+        st.ext_order = torch.from_numpy(rs.extend_order([r.cached for r in ext], lens)).to(device)
         st.table_ext = st.table_dev[:n_ext]
     if dec:
         st.q_dec = qtab.index_select(0, torch.from_numpy(np.concatenate(q_dec_idx)).to(device)).view(-1, Hq, D)
@@ -166,7 +167,7 @@ def run_extend(st):
     import radix_tree_prefix_amd as rs
     if st.ext:
         rs.extend_attention(st.q_ext, st.k_pool, st.v_pool, st.table_ext, st.qo_indptr, st.prefix_lens,
-                            st.extend_lens, st.max_ext, st.wl.sm_scale, out=st.out_ext)
+                            st.extend_lens, st.max_ext, st.wl.sm_scale, out=st.out_ext, order=st.ext_order)
 
 
 def run_decode(st, flat=False):

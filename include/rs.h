@@ -214,13 +214,20 @@ int rs_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new
  * q, out: device [sum(extend_lens)][Hq][D], requests packed in order (qo_indptr, device
  * int32 [B+1], gives each request's first query row).  prefix_lens, extend_lens: device
  * int32 [B]; req_to_token: device int32 [B][ld] with prefix+extend <= ld.
- * max_extend_len (host) bounds extend_lens and sizes the grid.  bf16: MFMA with fp32
- * accumulation; fp32: fp32 throughout. */
+ * max_extend_len (host) bounds extend_lens and sizes the grid.  order: device int32 [B],
+ * a permutation of 0..B-1 giving the order in which requests' work is started (longest
+ * first evens out the finish; rs_extend_order computes it), or NULL for 0..B-1; it changes
+ * no result.  bf16: MFMA with fp32 accumulation; fp32: fp32 throughout. */
 int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* req_to_token, int64_t ld, const int32_t* qo_indptr,
                         const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B,
                         int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
-                        int32_t dtype, void* out, void* stream);
+                        int32_t dtype, const int32_t* order, void* out, void* stream);
+
+/* Host: the request order for rs_extend_attention, longest causal work first
+ * (work = extend_len * (prefix_len + (extend_len + 1) / 2); ties by index).  prefix_lens,
+ * extend_lens: host int32 [B]; order: host int32 [B] out. */
+int rs_extend_order(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B, int32_t* order);
 
 /* Decode attention: one query per request at position seq_lens[b]-1 over positions
  * 0..seq_lens[b]-1 (its own KV stored first) [L "A quick recap"].  q, out: device

@@ -11,7 +11,7 @@ import torch
 
 from . import _lib
 from ._lib import (Tree, Plan, RsError, NoSpaceError, StaleError, DTYPE_F32, DTYPE_BF16,  # noqa: F401
-                   decode_workspace_bytes, LIB_PATH)
+                   decode_workspace_bytes, extend_order, LIB_PATH)
 
 __all__ = ["Tree", "Plan", "RsError", "NoSpaceError", "StaleError", "store_kv", "extend_attention",
            "decode_attention", "merge_states", "DecodeWorkspace", "LIB_PATH"]
@@ -46,8 +46,9 @@ def store_kv(k_pool, v_pool, k_new, v_new, slots, stream=None):
 
 
 def extend_attention(q, k_pool, v_pool, req_to_token, qo_indptr, prefix_lens, extend_lens, max_extend_len,
-                     sm_scale, out=None, stream=None):
-    """q [sum(ext), Hq, D]; req_to_token int32 [B, ld]; qo_indptr [B+1], prefix_lens/extend_lens [B] (device)."""
+                     sm_scale, out=None, order=None, stream=None):
+    """q [sum(ext), Hq, D]; req_to_token int32 [B, ld]; qo_indptr [B+1], prefix_lens/extend_lens [B] (device);
+    order: optional device int32 [B] start order (extend_order)."""
     T, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     B, ld = req_to_token.shape
@@ -56,12 +57,13 @@ def extend_attention(q, k_pool, v_pool, req_to_token, qo_indptr, prefix_lens, ex
                           _dev(req_to_token, "req_to_token", torch.int32), ld,
                           _dev(qo_indptr, "qo_indptr", torch.int32), _dev(prefix_lens, "prefix_lens", torch.int32),
                           _dev(extend_lens, "extend_lens", torch.int32), B, max_extend_len, Hq, Hkv, D, sm_scale,
-                          _dtype(k_pool), _dev(out, "out", k_pool.dtype), _stream(stream))
+                          _dtype(k_pool), _dev(out, "out", k_pool.dtype),
+                          order=_dev(order, "order", torch.int32) if order is not None else None, stream=_stream(stream))
     return out
 
 
 class DecodeWorkspace:
-    """Device workspace for rs_decode_attention (partials + completion counters), zeroed once."""
+    """Device workspace for rs_decode_attention (per-item partial outputs and lse)."""
 
     def __init__(self, plan, B, max_seq_len, Hq, Hkv, D, device="cuda", stream=None):
         self.nbytes = decode_workspace_bytes(plan, B, max_seq_len, Hq, Hkv, D)

@@ -95,7 +95,8 @@ _SIGS = {
     "rs_decode_workspace_init": (C.c_int, [_P, C.c_int64, _P]),
     "rs_store_kv": (C.c_int, [_P, _P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
     "rs_extend_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
-                                      C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P]),
+                                      C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P, _P]),
+    "rs_extend_order": (C.c_int, [_P, _P, C.c_int32, _P]),
     "rs_decode_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_float, C.c_int32, _P, _P, _P, C.c_int64, _P, _P, _P]),
     "rs_merge_states": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P]),
@@ -258,10 +259,19 @@ def store_kv(k_pool, v_pool, k_new, v_new, slots, n, Hkv, D, dtype, stream=0):
 
 
 def extend_attention(q, k_pool, v_pool, req_to_token, ld, qo_indptr, prefix_lens, extend_lens, B, max_extend_len,
-                     Hq, Hkv, D, sm_scale, dtype, out, stream=0):
+                     Hq, Hkv, D, sm_scale, dtype, out, order=None, stream=0):
     _check(lib.rs_extend_attention(q, k_pool, v_pool, req_to_token, int(ld), qo_indptr, prefix_lens, extend_lens,
                                    int(B), int(max_extend_len), int(Hq), int(Hkv), int(D), float(sm_scale),
-                                   int(dtype), out, C.c_void_p(stream)))
+                                   int(dtype), order, out, C.c_void_p(stream)))
+
+
+def extend_order(prefix_lens, extend_lens):
+    """Host: longest-work-first request order for extend_attention."""
+    p, pp = _i32(prefix_lens)
+    e, ep = _i32(extend_lens)
+    out = np.empty(len(p), np.int32)
+    _check(lib.rs_extend_order(pp, ep, len(p), out.ctypes.data_as(C.c_void_p)))
+    return out
 
 
 def decode_attention(q, k_pool, v_pool, req_to_token, ld, seq_lens, B, max_seq_len, Hq, Hkv, D, sm_scale, dtype,

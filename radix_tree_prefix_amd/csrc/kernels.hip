@@ -266,14 +266,16 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
-    int Hkv, float sm_scale, uint16_t* __restrict__ out) {
+    int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out) {
   __shared__ Stage<D> sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
   const int tpb = 128 / G;                        // tokens per tile
   const int kvh = blockIdx.x % Hkv;
   const int rest = blockIdx.x / Hkv;
-  const int qt = rest % n_qtiles, b = rest / n_qtiles;
+  // requests in the given order; within a request the later (longer) q-tiles first
+  const int qt = n_qtiles - 1 - rest % n_qtiles, i = rest / n_qtiles;
+  const int b = order ? order[i] : i;
   const int ext = extend_lens[b];
   const int t0 = qt * tpb;
   if (t0 >= ext) return;
@@ -657,7 +659,7 @@ int rs_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new
 int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
                         int64_t ld, const int32_t* qo_indptr, const int32_t* prefix_lens, const int32_t* extend_lens,
                         int32_t B, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
-                        int32_t dtype, void* out, void* stream) {
+                        int32_t dtype, const int32_t* order, void* out, void* stream) {
   if (B < 0 || max_extend_len < 0 || ld <= 0) return rs::fail(RS_E_INVAL, "rs_extend_attention: bad sizes");
   if (!dims_ok(Hq, Hkv, D)) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: heads/head_dim unsupported");
   if (B == 0 || max_extend_len == 0) return RS_OK;
@@ -672,7 +674,7 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     auto args = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
                          static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), req_to_token, ld,
-                         qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale,
+                         qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale, order,
                          static_cast<uint16_t*>(out));
     };
     if (D == 128) args(extend_bf16_kernel<128>);

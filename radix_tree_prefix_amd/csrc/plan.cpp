@@ -230,6 +230,18 @@ int rs_decode_plan_read(const rs_plan* p, void* host, int64_t bytes) {
 
 void rs_plan_destroy(rs_plan* p) { delete p; }
 
+int rs_extend_order(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B, int32_t* order) {
+  if (B < 0 || (B && (!prefix_lens || !extend_lens || !order))) return rs::fail(RS_E_INVAL, "rs_extend_order: bad arguments");
+  std::vector<std::pair<int64_t, int32_t>> w(B);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t e = extend_lens[b];
+    w[b] = {-(e * (int64_t(prefix_lens[b]) + (e + 1) / 2)), b};
+  }
+  std::sort(w.begin(), w.end());
+  for (int32_t b = 0; b < B; ++b) order[b] = w[b].second;
+  return RS_OK;
+}
+
 int64_t rs_decode_workspace_bytes(const rs_plan* p, int32_t B, int32_t max_seq_len, int32_t Hq,
                                   int32_t Hkv, int32_t D) {
   if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return rs::fail(RS_E_INVAL, "rs_decode_workspace_bytes: bad heads");

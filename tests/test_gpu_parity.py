@@ -346,3 +346,19 @@ def test_config5_mixed_batch_sampled(torch_rs):
         o, _ = _oracle_request(st, st.dec[i])
         worst = max(worst, float(np.abs(got[i] - o[0]).max()))
     assert worst <= TOL["bf16"], ("decode", worst)
+
+
+def test_extend_order_changes_no_result(torch_rs):
+    """The longest-first start order only reorders workgroups: outputs are bit-identical."""
+    torch, rs = torch_rs
+    _say("config 3 extend with and without the work order")
+    b = _bench()
+    st = b.setup(3)
+    b.run_store(st)
+    b.run_extend(st)
+    with_order = st.out_ext.clone()
+    rs.extend_attention(st.q_ext, st.k_pool, st.v_pool, st.table_ext, st.qo_indptr, st.prefix_lens,
+                        st.extend_lens, st.max_ext, st.wl.sm_scale, out=st.out_ext)
+    torch.cuda.synchronize()
+    assert torch.equal(with_order, st.out_ext)
+    assert sorted(st.ext_order.cpu().tolist()) == list(range(len(st.ext)))
