@@ -27,6 +27,7 @@
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <utility>
 
 #include "internal.h"
 #include "plan.h"
@@ -41,6 +42,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kBN = 64;       // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;   // softmax weights stay below 2^kSlack between rescales
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
@@ -53,8 +55,8 @@ __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a,
 
 // One stage of a K/V tile in LDS: kBN key rows of K and of V, row-major, rows padded
 // (K: +16 bytes, V: +32 bytes) so that the MFMA operand reads below hit distinct banks.
-// Rows arrive straight from global memory: one global_load_lds_dword per row, the 64
-// lanes of a wave covering the row's Hkv-slice (256 bytes at d=128) -- a fully
+// Rows arrive straight from global memory: one dword buffer load into LDS per row, the
+// 64 lanes of a wave covering the row's Hkv-slice (256 bytes at d=128) -- a fully
 // coalesced request with a wave-uniform slot -- and no staging registers or LDS writes.
 template <int D>
 struct StageLayout {
@@ -70,23 +72,48 @@ struct __align__(16) Stage {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Slot ids of this wave's kBN/4 rows of the tile at key0: lane l holds the slot of row
+// l%16.  Keys past k1 repeat the slot
+// of key k1-1 -- an in-bounds row whose scores the caller masks.
+constexpr int kRowsPerWave = kBN / 4;
+
+__device__ __forceinline__ int wave_slots(const int32_t* __restrict__ trow, int key0, int k1, int wave_u, int lane) {
+  return trow[min(key0 + wave_u * kRowsPerWave + (lane & 15), k1 - 1)];
+}
+
 // Issue the global->LDS loads of one tile: wave w fills key rows [w*kBN/4, (w+1)*kBN/4)
-// of K and of V; sreg = tile_slots (lane t holds key t's slot).
-template <int D>
-__device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* __restrict__ kp,
-                                           const uint16_t* __restrict__ vp, int sreg, uint32_t slot_stride,
-                                           int lane, int wave_u) {
-  constexpr int RPW = kBN / 4;                        // rows per wave
+// of K and of V.  Each row is one buffer_load_dword ... lds: its slot comes to a scalar
+// register (readlane), the row's 64-bit address and a raw buffer descriptor over its
+// D*2 bytes are formed in scalar registers, and the 64 lanes fetch one dword each
+// (voff = 4*lane; lanes past D/2 are switched off for d=64 so they write nothing into
+// the next LDS row).  Buffer offsets are 32-bit, so the base moves per row: a pool may
+// be larger than 4 GiB.
+constexpr int kBufferWord3 = 0x00020000;   // 32-bit data format, no swizzle
+
+template <int D, int I>
+__device__ __forceinline__ void issue_row(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
+                                          int slots, uint32_t voff, int wave_u) {
   using L = StageLayout<D>;
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int r = wave_u * RPW + i;
-    const uint64_t row = uint64_t(uint32_t(__builtin_amdgcn_readlane(sreg, r))) * slot_stride;
-    if (D == 128 || lane < D / 2) {
-      __builtin_amdgcn_global_load_lds(kp + row + 2 * lane, (lds_ptr)(dst.k + r * L::kK), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + row + 2 * lane, (lds_ptr)(dst.v + r * L::kV), 4, 0, 0);
-    }
-  }
+  const int r = wave_u * kRowsPerWave + I;
+  const uint64_t off = uint64_t(uint32_t(__builtin_amdgcn_readlane(slots, I))) * row_bytes;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), (short)0, D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), (short)0, D * 2, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(dst.k + r * L::kK), 4, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr)(dst.v + r * L::kV), 4, voff, 0, 0, 0);
+}
+
+template <int D, int... I>
+__device__ __forceinline__ void issue_rows(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
+                                           int slots, uint32_t voff, int wave_u, std::integer_sequence<int, I...>) {
+  (issue_row<D, I>(dst, kp, vp, row_bytes, slots, voff, wave_u), ...);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* kp, const uint16_t* vp, uint32_t row_bytes,
+                                           int slots, uint32_t voff, int lane, int wave_u) {
+  if (D == 128 || lane < D / 2)
+    issue_rows<D>(dst, reinterpret_cast<const char*>(kp), reinterpret_cast<const char*>(vp), row_bytes, slots, voff,
+                  wave_u, std::make_integer_sequence<int, kRowsPerWave>{});
 }
 
 // ------------------------------------------------------------------ per-wave math
@@ -94,7 +121,8 @@ __device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* __rest
 template <int D>
 struct WaveState {
   f32x16 o[D / 32];     // O^T accumulators: o[mb][j] = O[row][mb*32 + 8*(j/4) + 4*(lane/32) + j%4]
-  float m;              // running max of raw scores (-inf before any visible key)
+  float m;              // reference point of the exponentials, in raw score units: at most
+                        // kSlack/c below the running max (-inf before any visible key)
   float l;              // this lane's half of the running sum of exp2((s - m) * c)
 };
 
@@ -123,9 +151,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
 // visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
+// c = sm_scale*log2(e); slack = kSlack / c (the same margin in raw score units).
 template <int D>
 __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
-                                          int lane, bool mask, int nk, int key_pos0, int lim, float c) {
+                                          int lane, bool mask, int nk, int key_pos0, int lim, float c, float slack) {
   using L = StageLayout<D>;
   const int r32 = lane & 31, hi = lane >> 5;
   const char* kb = sm.k + r32 * L::kK + hi * 16;         // key r32, elements 16ks + 8hi ..
@@ -155,30 +184,32 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb32][j]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(ws.m, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  // v_exp_f32 directly: results below 2^-126 flush to zero, which softmax weights can afford
-  const float alpha = __builtin_amdgcn_exp2f((ws.m - m_use) * c);
-  const float mc = m_use * c;
-  float sum = 0.f;
+  // The reference point m of the exponentials moves only when some row's maximum
+  // exceeds it by more than kSlack (in exp2 units), so weights stay below 2^kSlack and
+  // most tiles skip the rescale of O and l; softmax does not depend on the point.
+  if (__builtin_amdgcn_ballot_w64(mx > ws.m + slack)) {
+    const float m_new = fmaxf(ws.m, mx);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    // v_exp_f32 directly: results below 2^-126 flush to zero, which softmax weights can afford
+    const float alpha = __builtin_amdgcn_exp2f((ws.m - m_ref) * c);
+    ws.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ws.o[mb][j] *= alpha;
+    ws.m = m_new;
+  }
+  const float mc = (ws.m == -INFINITY ? 0.f : ws.m) * c;
 #pragma unroll
   for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
-      s[kb32][j] = p;
-      sum += p;
-    }
-  ws.l = fmaf(ws.l, alpha, sum);
-  ws.m = m_new;
-#pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ws.o[mb][j] *= alpha;
+    for (int j = 0; j < 16; ++j) s[kb32][j] = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
   // V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
   // element i%4 of the 8-byte pieces read by lanes i/4 + 4k (k = 0..3).  Provider lane j
   // reads key kbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
   // V[kbase + k][dbase + i], k = 0..3: the four keys of its P^T slots 4r..4r+3.
+  const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+  float sum = 0.f;
   const int i16 = lane & 15, gpar = (lane >> 4) & 1;
   const char* vb = sm.v + (hi * 4 + (i16 >> 2)) * L::kV + (16 * gpar + 4 * (i16 & 3)) * 2;
 #pragma unroll
@@ -190,6 +221,11 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     pu.z = pack_bf16(s[kb32][h8 + 4], s[kb32][h8 + 5]);
     pu.w = pack_bf16(s[kb32][h8 + 6], s[kb32][h8 + 7]);
     const bf16x8 b = __builtin_bit_cast(bf16x8, pu);
+    // the row sum of the weights as the second MFMA sees them (bf16), two per dot2
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.x), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.y), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.z), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.w), kOnes, sum, false);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       const char* p0 = vb + kstep * 16 * L::kV + mb * 64;
@@ -200,12 +236,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
       ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
     }
   }
-}
-
-// Slot ids of one tile, clamped: lane l holds the slot of key min(key0 + l, k1 - 1).
-// Keys past the range repeat the last valid slot (an in-bounds row); they are masked.
-__device__ __forceinline__ int clamped_slots(const int32_t* __restrict__ trow, int key0, int k1, int lane) {
-  return trow[min(key0 + lane, k1 - 1)];
+  ws.l += sum;
 }
 
 template <int N>
@@ -228,17 +259,20 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 template <int D, int NS, bool SKIP_EMPTY>
 __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-                                            const int32_t* __restrict__ trow, uint32_t slot_stride, int k0, int k1,
+                                            const int32_t* __restrict__ trow, int Hkv, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
   if (k0 >= k1) return;
-  constexpr int kDmaPerTile = 2 * (kBN / 4);          // K + V rows one wave issues per tile
+  constexpr int kDmaPerTile = 2 * kRowsPerWave;       // K + V rows one wave issues per tile
   const int lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t voff = uint32_t(lane) * 4u;
+  const float slack = kSlack / c;
+  const uint32_t row_bytes = uint32_t(Hkv) * D * 2;
   const int ntiles = (k1 - k0 + kBN - 1) / kBN;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < ntiles) issue_tile<D>(sm[j], kp, vp, clamped_slots(trow, k0 + j * kBN, k1, lane), slot_stride, lane, wave_u);
-  int s_next = clamped_slots(trow, k0 + (NS - 1) * kBN, k1, lane);
+    if (j < ntiles) issue_tile<D>(sm[j], kp, vp, row_bytes, wave_slots(trow, k0 + j * kBN, k1, wave_u, lane), voff, lane, wave_u);
+  int s_next = wave_slots(trow, k0 + (NS - 1) * kBN, k1, wave_u, lane);
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = k0 + t * kBN;
     const int nk = min(kBN, k1 - key0);
@@ -249,13 +283,12 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS]
     if (NS > 2 && t + NS - 2 < ntiles && t >= NS - 2) wait_vmcnt_barrier<kAfter>();
     else wait_vmcnt_barrier<0>();
     if (t + NS - 1 < ntiles) {
-      const int s_after = clamped_slots(trow, k0 + (t + NS) * kBN, k1, lane);
-      issue_tile<D>(sm[(t + NS - 1) % NS], kp, vp, s_next, slot_stride, lane, wave_u);
-      s_next = s_after;
+      issue_tile<D>(sm[(t + NS - 1) % NS], kp, vp, row_bytes, s_next, voff, lane, wave_u);
+      s_next = wave_slots(trow, k0 + (t + NS) * kBN, k1, wave_u, lane);
     }
     if (!SKIP_EMPTY || has_rows) {
       const bool mask = nk < kBN || key0 + kBN > mask_from;
-      wave_tile<D>(ws, sm[t % NS], qf, lane, mask, nk, key0, lim, c);
+      wave_tile<D>(ws, sm[t % NS], qf, lane, mask, nk, key0, lim, c, slack);
     }
   }
 }
@@ -296,7 +329,7 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
   const bool has_rows = wave * 32 < ntok * G;
   const float c = sm_scale * kLog2e;
   stream_keys<D, 2, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
-                 uint32_t(Hkv * D), 0, key_end, mask_from, lim, c, has_rows, tid);
+                 Hkv, 0, key_end, mask_from, lim, c, has_rows, tid);
   if (!valid) return;
   float l = ws.l + __shfl_xor(ws.l, 32);
   float inv = l > 0.f ? 1.f / l : 0.f;
@@ -389,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   wave_init<D>(ws);
   const bool has_rows = wave * 32 < nreq * G;
   stream_keys<D, 2, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
-                 a.req_to_token + int64_t(rep) * a.ld, uint32_t(a.Hkv * D), k0, k1, k1, INT32_MAX,
+                 a.req_to_token + int64_t(rep) * a.ld, a.Hkv, k0, k1, k1, INT32_MAX,
                  a.sm_scale * kLog2e, has_rows, tid);
   if (!valid) return;
   const float l = ws.l + __shfl_xor(ws.l, 32);
