@@ -53,15 +53,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
-// One stage of a K/V tile in LDS: kBN key rows of K and of V, row-major, rows padded
-// (K: +16 bytes, V: +32 bytes) so that the MFMA operand reads below hit distinct banks.
+// One stage of a K/V tile in LDS: kBN key rows of K and of V, row-major, rows padded so
+// that the MFMA operand reads below hit distinct banks of the 64 x 4-byte LDS banks:
+// K (+16 bytes): the 16 rows of a ds_read_b128 phase start 4 banks apart; V (+64
+// bytes): the 4 rows of a transposing ds_read_b64 phase start 16 banks apart.
 // Rows arrive straight from global memory: one dword buffer load into LDS per row, the
 // 64 lanes of a wave covering the row's Hkv-slice (256 bytes at d=128) -- a fully
 // coalesced request with a wave-uniform slot -- and no staging registers or LDS writes.
 template <int D>
 struct StageLayout {
   static constexpr int kK = D * 2 + 16;       // K row stride (bytes)
-  static constexpr int kV = D * 2 + 32;       // V row stride (bytes)
+  static constexpr int kV = D * 2 + 64;       // V row stride (bytes)
 };
 
 template <int D>
