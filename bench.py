@@ -69,7 +69,8 @@ def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
     st.history_s = time.perf_counter() - t0
 
     # batch: admit every request in order, its slots straight into its table row
-    ld = max(r.seq_len for r in wl.requests)
+    # table rows padded to 64 bytes, as an engine allocates its request-to-token pool
+    ld = -(-max(r.seq_len for r in wl.requests) // 16) * 16
     table = np.full((wl.B, ld), -1, np.int32)
     nodes = np.zeros(wl.B, np.int64)
     matched = np.zeros(wl.B, np.int64)

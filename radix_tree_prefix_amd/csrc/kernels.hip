@@ -53,69 +53,88 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
-// One stage of a K/V tile in LDS: kBN key rows of K and of V, row-major, rows padded so
-// that the MFMA operand reads below hit distinct banks of the 64 x 4-byte LDS banks:
-// K (+16 bytes): the 16 rows of a ds_read_b128 phase start 4 banks apart; V (+64
-// bytes): the 4 rows of a transposing ds_read_b64 phase start 16 banks apart.
-// Rows arrive straight from global memory: one dword buffer load into LDS per row, the
-// 64 lanes of a wave covering the row's Hkv-slice (256 bytes at d=128) -- a fully
-// coalesced request with a wave-uniform slot -- and no staging registers or LDS writes.
+// One stage of a K/V tile in LDS: kBN rows of K and of V, D*2 bytes each, unpadded.
+// Rows arrive straight from global memory with global_load_lds_dwordx4: one instruction
+// moves kRowsPerInst whole rows (lane l writes 16 bytes at M0 + 16*l), every lane with
+// its own 64-bit source address -- a fully coalesced request, no staging registers.
+//
+// Two permutations make this work with the 64 x 4-byte LDS banks:
+// * rows: instruction g of wave w fills LDS rows 16w + kRowsPerInst*g + j (j < rows per
+//   instruction), holding keys 16w + g + kInstPerWave*j, so a lane's kInstPerWave slot
+//   ids are consecutive table entries (one load) -- key_of_row() undoes it for masking;
+// * 16-byte chunks: chunk c of LDS row R sits at position c ^ swz(R), which spreads the
+//   16 rows of a K-operand ds_read_b128 phase and the 4 rows x 4 chunks of a V-operand
+//   transposing ds_read_b64 phase over distinct banks (no conflicts).
 template <int D>
 struct StageLayout {
-  static constexpr int kK = D * 2 + 16;       // K row stride (bytes)
-  static constexpr int kV = D * 2 + 64;       // V row stride (bytes)
+  static constexpr int kRow = D * 2;                  // bytes per row (K and V)
+  static constexpr int kChunks = kRow / 16;           // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;   // rows one dwordx4 DMA instruction fills
+  static constexpr int kInstPerWave = kBN / 4 / kRowsPerInst;
 };
 
 template <int D>
 struct __align__(16) Stage {
-  char k[kBN * StageLayout<D>::kK];
-  char v[kBN * StageLayout<D>::kV];
+  char k[kBN * StageLayout<D>::kRow];
+  char v[kBN * StageLayout<D>::kRow];
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Slot ids of this wave's kBN/4 rows of the tile at key0: lane l holds the slot of row
-// l%16.  Keys past k1 repeat the slot
-// of key k1-1 -- an in-bounds row whose scores the caller masks.
-constexpr int kRowsPerWave = kBN / 4;
-
-__device__ __forceinline__ int wave_slots(const int32_t* __restrict__ trow, int key0, int k1, int wave_u, int lane) {
-  return trow[min(key0 + wave_u * kRowsPerWave + (lane & 15), k1 - 1)];
-}
-
-// Issue the global->LDS loads of one tile: wave w fills key rows [w*kBN/4, (w+1)*kBN/4)
-// of K and of V.  Each row is one buffer_load_dword ... lds: its slot comes to a scalar
-// register (readlane), the row's 64-bit address and a raw buffer descriptor over its
-// D*2 bytes are formed in scalar registers, and the 64 lanes fetch one dword each
-// (voff = 4*lane; lanes past D/2 are switched off for d=64 so they write nothing into
-// the next LDS row).  Buffer offsets are 32-bit, so the base moves per row: a pool may
-// be larger than 4 GiB.
-constexpr int kBufferWord3 = 0x00020000;   // 32-bit data format, no swizzle
-
-template <int D, int I>
-__device__ __forceinline__ void issue_row(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
-                                          int slots, uint32_t voff, int wave_u) {
-  using L = StageLayout<D>;
-  const int r = wave_u * kRowsPerWave + I;
-  const uint64_t off = uint64_t(uint32_t(__builtin_amdgcn_readlane(slots, I))) * row_bytes;
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + off), (short)0, D * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + off), (short)0, D * 2, kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr)(dst.k + r * L::kK), 4, voff, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr)(dst.v + r * L::kV), 4, voff, 0, 0, 0);
-}
-
-template <int D, int... I>
-__device__ __forceinline__ void issue_rows(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
-                                           int slots, uint32_t voff, int wave_u, std::integer_sequence<int, I...>) {
-  (issue_row<D, I>(dst, kp, vp, row_bytes, slots, voff, wave_u), ...);
+template <int D>
+__device__ __forceinline__ int swz(int R) {
+  return D == 128 ? 4 * (R & 3) + ((R >> 2) & 3) : 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
 }
 
 template <int D>
-__device__ __forceinline__ void issue_tile(Stage<D>& dst, const uint16_t* kp, const uint16_t* vp, uint32_t row_bytes,
-                                           int slots, uint32_t voff, int lane, int wave_u) {
-  if (D == 128 || lane < D / 2)
-    issue_rows<D>(dst, reinterpret_cast<const char*>(kp), reinterpret_cast<const char*>(vp), row_bytes, slots, voff,
-                  wave_u, std::make_integer_sequence<int, kRowsPerWave>{});
+__device__ __forceinline__ int key_of_row(int R) {
+  return D == 128 ? (R & ~15) | ((R & 15) >> 2) | ((R & 3) << 2) : (R & ~15) | ((R & 15) >> 3) | ((R & 7) << 1);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+constexpr int kRowsPerWave = kBN / 4;
+
+// Slot ids for this lane's DMA rows of the tile at key0: s[g] = slot of key
+// key0 + 16w + kInstPerWave*j + g (j = lane / chunks per row).  Keys past k1 repeat the
+// slot of key k1-1 -- an in-bounds row whose scores the caller masks.
+template <int D>
+struct TileSlots {
+  int s[StageLayout<D>::kInstPerWave];
+};
+
+template <int D>
+__device__ __forceinline__ TileSlots<D> wave_slots(const int32_t* __restrict__ trow, int key0, int k1, int wave_u,
+                                                   int lane) {
+  using L = StageLayout<D>;
+  typedef int slots_vec __attribute__((ext_vector_type(L::kInstPerWave)));
+  TileSlots<D> t;
+  const int base = key0 + wave_u * kRowsPerWave;
+  const int k = base + L::kInstPerWave * (lane / L::kChunks);
+  // one vector load per lane when every row is in range and the entries are aligned for it
+  if (base + kRowsPerWave <= k1 && (reinterpret_cast<uintptr_t>(trow + base) & (4 * L::kInstPerWave - 1)) == 0) {
+    const slots_vec v = *reinterpret_cast<const slots_vec*>(trow + k);
+#pragma unroll
+    for (int g = 0; g < L::kInstPerWave; ++g) t.s[g] = v[g];
+  } else {
+#pragma unroll
+    for (int g = 0; g < L::kInstPerWave; ++g) t.s[g] = trow[min(k + g, k1 - 1)];
+  }
+  return t;
+}
+
+// Issue the global->LDS loads of one tile (this wave's kBN/4 rows of K and of V).
+// co[g] = this lane's byte offset within its row for instruction g (its swizzled chunk).
+template <int D>
+__device__ __forceinline__ void issue_tile(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
+                                           const TileSlots<D>& ts, const uint32_t (&co)[StageLayout<D>::kInstPerWave],
+                                           int wave_u) {
+  using L = StageLayout<D>;
+#pragma unroll
+  for (int g = 0; g < L::kInstPerWave; ++g) {
+    const uint64_t off = uint64_t(uint32_t(ts.s[g])) * row_bytes + co[g];
+    const int r0 = wave_u * kRowsPerWave + g * L::kRowsPerInst;
+    __builtin_amdgcn_global_load_lds(kp + off, (lds_ptr)(dst.k + r0 * L::kRow), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + off, (lds_ptr)(dst.v + r0 * L::kRow), 16, 0, 0);
+  }
 }
 
 // ------------------------------------------------------------------ per-wave math
@@ -153,13 +172,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
 // visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
+// The math runs over LDS rows; the key of a row only matters for the mask.
 // c = sm_scale*log2(e); slack = kSlack / c (the same margin in raw score units).
 template <int D>
 __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
                                           int lane, bool mask, int nk, int key_pos0, int lim, float c, float slack) {
   using L = StageLayout<D>;
   const int r32 = lane & 31, hi = lane >> 5;
-  const char* kb = sm.k + r32 * L::kK + hi * 16;         // key r32, elements 16ks + 8hi ..
+  const char* kb = sm.k + r32 * L::kRow;                 // LDS row r32 (and r32 + 32)
+  const int fk = swz<D>(r32);                            // rows r32, r32 + 32 share it
   f32x16 s[2];
 #pragma unroll
   for (int kb32 = 0; kb32 < 2; ++kb32) {
@@ -167,7 +188,8 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     for (int j = 0; j < 16; ++j) s[kb32][j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + kb32 * 32 * L::kK + ks * 32);
+      // elements 16ks + 8hi .. +8 of the row = 16-byte chunk 2ks + hi
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + kb32 * 32 * L::kRow + 16 * ((2 * ks + hi) ^ fk));
       s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb32], 0, 0, 0);
     }
   }
@@ -176,7 +198,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     for (int kb32 = 0; kb32 < 2; ++kb32)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int t = kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        const int t = key_of_row<D>(kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3));
         if (t >= nk || key_pos0 + t > lim) s[kb32][j] = -INFINITY;
       }
   }
@@ -208,12 +230,18 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     for (int j = 0; j < 16; ++j) s[kb32][j] = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
   // V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
   // element i%4 of the 8-byte pieces read by lanes i/4 + 4k (k = 0..3).  Provider lane j
-  // reads key kbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
-  // V[kbase + k][dbase + i], k = 0..3: the four keys of its P^T slots 4r..4r+3.
+  // reads row rbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
+  // V[rbase + k][dbase + i], k = 0..3: the four rows of its P^T slots 4r..4r+3.
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
   float sum = 0.f;
   const int i16 = lane & 15, gpar = (lane >> 4) & 1;
-  const char* vb = sm.v + (hi * 4 + (i16 >> 2)) * L::kV + (16 * gpar + 4 * (i16 & 3)) * 2;
+  // this lane's rows hi*4 + i16/4 (+8, +16*kstep) at bytes 32gpar + 8(i16%4) + 64mb:
+  // chunk 2gpar + (i16%4)/2 + 4mb, half i16%2; the swizzle depends on the row mod 16
+  const int vr0 = hi * 4 + (i16 >> 2);
+  const int cv = 2 * gpar + ((i16 & 3) >> 1);
+  const int fv0 = swz<D>(vr0), fv1 = swz<D>(vr0 + 8);
+  const char* vb0 = sm.v + vr0 * L::kRow + 8 * (i16 & 1);
+  const char* vb1 = vb0 + 8 * L::kRow;
 #pragma unroll
   for (int kstep = 0; kstep < 4; ++kstep) {
     const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
@@ -230,9 +258,10 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
     sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.w), kOnes, sum, false);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      const char* p0 = vb + kstep * 16 * L::kV + mb * 64;
+      const char* p0 = vb0 + kstep * 16 * L::kRow + 16 * ((cv + 4 * mb) ^ fv0);
+      const char* p1 = vb1 + kstep * 16 * L::kRow + 16 * ((cv + 4 * mb) ^ fv1);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 8 * L::kV));
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
       const bf16x8 a = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
           lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
       ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
@@ -258,41 +287,79 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // t-1 used); it then issues the slot ids of tile t+NS and the loads of tile t+NS-1 into
 // that stage, and computes tile t.  While tile t+1 is in flight the wait leaves exactly
 // the loads issued after tile t's (one iteration's worth) outstanding.
+template <int D>
+struct StreamArgs {
+  const char* kc;
+  const char* vc;
+  const int32_t* trow;
+  uint32_t row_bytes;
+  uint32_t co[StageLayout<D>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
+  int k0, k1, ntiles, mask_from, lim, wave_u, lane;
+  float c, slack;
+  bool has_rows;
+};
+
+// Iteration t of the pipeline; its tile sits in stage t % NS.
+template <int D, int NS, bool SKIP_EMPTY>
+__device__ __forceinline__ void stream_step(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
+                                            const StreamArgs<D>& a, TileSlots<D>& s_next, int t) {
+  using L = StageLayout<D>;
+  // K + V DMA and the next slot loads (one vector load, or kInstPerWave single loads):
+  // at least this many per iteration
+  constexpr int kPerIter = 2 * L::kInstPerWave + 1;
+  const int key0 = a.k0 + t * kBN;
+  const int nk = min(kBN, a.k1 - key0);
+  // After tile t's loads came, in order: the next tiles' (issued one iteration each, at
+  // least kPerIter instructions per iteration) -- exactly when all of them exist.
+  // (vmcnt counts to 63: a smaller count only waits a little longer)
+  constexpr int kAfter = (NS - 2) * kPerIter < 63 ? (NS - 2) * kPerIter : 63;
+  if (NS > 2 && t + NS - 2 < a.ntiles && t >= NS - 2) wait_vmcnt_barrier<kAfter>();
+  else wait_vmcnt_barrier<0>();
+  if (t + NS - 1 < a.ntiles) {
+    issue_tile<D>(sm[(t + NS - 1) % NS], a.kc, a.vc, a.row_bytes, s_next, a.co, a.wave_u);
+    s_next = wave_slots<D>(a.trow, a.k0 + (t + NS) * kBN, a.k1, a.wave_u, a.lane);
+  }
+  if (!SKIP_EMPTY || a.has_rows) {
+    const bool mask = nk < kBN || key0 + kBN > a.mask_from;
+    wave_tile<D>(ws, sm[t % NS], qf, a.lane, mask, nk, key0, a.lim, a.c, a.slack);
+  }
+}
+
+
 template <int D, int NS, bool SKIP_EMPTY>
 __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                                             const int32_t* __restrict__ trow, int Hkv, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
   if (k0 >= k1) return;
-  constexpr int kDmaPerTile = 2 * kRowsPerWave;       // K + V rows one wave issues per tile
-  const int lane = tid & 63;
-  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t voff = uint32_t(lane) * 4u;
-  const float slack = kSlack / c;
-  const uint32_t row_bytes = uint32_t(Hkv) * D * 2;
-  const int ntiles = (k1 - k0 + kBN - 1) / kBN;
+  using L = StageLayout<D>;
+  StreamArgs<D> a;
+  a.kc = reinterpret_cast<const char*>(kp);
+  a.vc = reinterpret_cast<const char*>(vp);
+  a.trow = trow;
+  a.row_bytes = uint32_t(Hkv) * D * 2;
+  a.lane = tid & 63;
+  a.wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this lane's source byte offset within its row for each DMA instruction: the chunk
+  // that belongs at its LDS position (the swizzle depends on the LDS row mod 16)
+#pragma unroll
+  for (int g = 0; g < L::kInstPerWave; ++g)
+    a.co[g] = 16u * uint32_t((a.lane % L::kChunks) ^ swz<D>(g * L::kRowsPerInst + a.lane / L::kChunks));
+  a.k0 = k0;
+  a.k1 = k1;
+  a.ntiles = (k1 - k0 + kBN - 1) / kBN;
+  a.mask_from = mask_from;
+  a.lim = lim;
+  a.c = c;
+  a.slack = kSlack / c;
+  a.has_rows = has_rows;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < ntiles) issue_tile<D>(sm[j], kp, vp, row_bytes, wave_slots(trow, k0 + j * kBN, k1, wave_u, lane), voff, lane, wave_u);
-  int s_next = wave_slots(trow, k0 + (NS - 1) * kBN, k1, wave_u, lane);
-  for (int t = 0; t < ntiles; ++t) {
-    const int key0 = k0 + t * kBN;
-    const int nk = min(kBN, k1 - key0);
-    // After tile t's loads came, in order: the next tiles' (issued one iteration each,
-    // kDmaPerTile + 1 instructions per iteration) -- exactly when all of them exist.
-    // (vmcnt counts to 63: a smaller count only waits a little longer)
-    constexpr int kAfter = (NS - 2) * (kDmaPerTile + 1) < 63 ? (NS - 2) * (kDmaPerTile + 1) : 63;
-    if (NS > 2 && t + NS - 2 < ntiles && t >= NS - 2) wait_vmcnt_barrier<kAfter>();
-    else wait_vmcnt_barrier<0>();
-    if (t + NS - 1 < ntiles) {
-      issue_tile<D>(sm[(t + NS - 1) % NS], kp, vp, row_bytes, s_next, voff, lane, wave_u);
-      s_next = wave_slots(trow, k0 + (t + NS) * kBN, k1, wave_u, lane);
-    }
-    if (!SKIP_EMPTY || has_rows) {
-      const bool mask = nk < kBN || key0 + kBN > mask_from;
-      wave_tile<D>(ws, sm[t % NS], qf, lane, mask, nk, key0, lim, c, slack);
-    }
-  }
+    if (j < a.ntiles)
+      issue_tile<D>(sm[j], a.kc, a.vc, a.row_bytes, wave_slots<D>(trow, k0 + j * kBN, k1, a.wave_u, a.lane), a.co,
+                    a.wave_u);
+  TileSlots<D> s_next = wave_slots<D>(trow, k0 + (NS - 1) * kBN, k1, a.wave_u, a.lane);
+  for (int t = 0; t < a.ntiles; ++t) stream_step<D, NS, SKIP_EMPTY>(ws, sm, qf, a, s_next, t);
 }
 
 // ------------------------------------------------------------------ extend (bf16)
