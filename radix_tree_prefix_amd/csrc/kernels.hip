@@ -529,35 +529,59 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
 
 // Log-sum-exp merge of each (request, KV head)'s partials:
 //   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
-// The weights of up to kMergeBatch partials per head are computed once into LDS; then each
-// thread accumulates its output elements with independent, coalesced partial loads.
+// Per group of up to 16 query heads: each wave reduces the max and the sum of its heads'
+// lse over the partials (64 partials per step, lane-parallel); the weights of a batch of
+// kMergeBatch partials go to LDS; then every thread accumulates its output elements over
+// the batch, four partials per step so their loads are in flight together.
 constexpr int kMergeBatch = 64;
+constexpr int kMergeHeads = 16;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[16 * kMergeBatch];            // weights [g][i], 16 heads per pass
+  __shared__ float s_w[kMergeHeads * kMergeBatch];   // weights [g][i] of the current batch
   __shared__ int s_p[kMergeBatch];
-  __shared__ float s_m[16], s_sum[16];
+  __shared__ float s_m[kMergeHeads], s_sum[kMergeHeads];
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const PartList pl = part_list(a, b);
   if (pl.n <= 1) return;
   const int G = a.Hq / a.Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
   const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
-  for (int g0 = 0; g0 < G; g0 += 16) {                 // groups of up to 16 query heads
-    const int ng = min(16, G - g0);
-    // pass 1: running max and sum over all partials, per head
-    if (tid < ng) {
-      float mx = -INFINITY;
-      for (int i = 0; i < pl.n; ++i) mx = fmaxf(mx, lp[int64_t(pl.at(i)) * G + g0 + tid]);
-      float sum = 0.f;
-      for (int i = 0; i < pl.n; ++i) sum += __expf(lp[int64_t(pl.at(i)) * G + g0 + tid] - mx);
-      s_m[tid] = mx;
-      s_sum[tid] = sum;
+  for (int g0 = 0; g0 < G; g0 += kMergeHeads) {
+    const int ng = min(kMergeHeads, G - g0);
+    // pass 1: max and sum of exp over all partials, one head per wave at a time
+    for (int g = wave; g < ng; g += kThreads / 64) {
+      float m = -INFINITY, sum = 0.f;
+      for (int i0 = 0; i0 < pl.n; i0 += 64) {
+        const int i = i0 + lane;
+        const float v = i < pl.n ? lp[int64_t(pl.at(i)) * G + g0 + g] : -INFINITY;
+        const float m_new = fmaxf(m, wave_max(v));
+        if (m_new != -INFINITY) {
+          sum = sum * __expf(m - m_new) + wave_sum(__expf(v - m_new));
+          m = m_new;
+        }
+      }
+      if (lane == 0) {
+        s_m[g] = m;
+        s_sum[g] = sum;
+      }
     }
     __syncthreads();
-    constexpr int kPer = 16 * D / kThreads;             // elements per thread (8 at d128)
+    constexpr int kPer = kMergeHeads * D / kThreads;   // element slots per thread
+    const int n_el = ng * D;
     float acc[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
@@ -570,13 +594,31 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
         s_w[g * kMergeBatch + i] = __expf(lp[int64_t(s_p[i]) * G + g0 + g] - s_m[g]) / s_sum[g];
       }
       __syncthreads();
-      for (int i = 0; i < nb; ++i) {
+      int i = 0;
+      for (; i + 4 <= nb; i += 4) {
+        const float* src0 = op + (int64_t(s_p[i + 0]) * G + g0) * D;
+        const float* src1 = op + (int64_t(s_p[i + 1]) * G + g0) * D;
+        const float* src2 = op + (int64_t(s_p[i + 2]) * G + g0) * D;
+        const float* src3 = op + (int64_t(s_p[i + 3]) * G + g0) * D;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int idx = tid + e * kThreads;            // (g, d) flattened
+          if (idx < n_el) {
+            const float* w = s_w + (idx / D) * kMergeBatch + i;
+            const float x0 = src0[idx], x1 = src1[idx], x2 = src2[idx], x3 = src3[idx];
+            acc[e] = fmaf(w[0], x0, acc[e]);
+            acc[e] = fmaf(w[1], x1, acc[e]);
+            acc[e] = fmaf(w[2], x2, acc[e]);
+            acc[e] = fmaf(w[3], x3, acc[e]);
+          }
+        }
+      }
+      for (; i < nb; ++i) {
         const float* src = op + (int64_t(s_p[i]) * G + g0) * D;
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
-          const int idx = tid + e * kThreads;            // (g, d) flattened, g < 16
-          const int g = idx / D;
-          if (g < ng) acc[e] = fmaf(s_w[g * kMergeBatch + i], src[idx], acc[e]);
+          const int idx = tid + e * kThreads;
+          if (idx < n_el) acc[e] = fmaf(s_w[(idx / D) * kMergeBatch + i], src[idx], acc[e]);
         }
       }
       __syncthreads();
@@ -584,8 +626,8 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int idx = tid + e * kThreads;
-      const int g = idx / D, d = idx % D;
-      if (g < ng) {
+      if (idx < n_el) {
+        const int g = idx / D, d = idx % D;
         const int64_t orow = int64_t(b) * a.Hq + kvh * G + g0 + g;
         a.out[orow * D + d] = f2bf(acc[e]);
         if (d == 0 && a.lse_out) a.lse_out[orow] = s_m[g] + __logf(s_sum[g]);
