@@ -40,7 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kBN = 64;       // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;   // softmax weights stay below 2^kSlack between rescales
 
@@ -53,30 +52,33 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
-// One stage of a K/V tile in LDS: kBN rows of K and of V, D*2 bytes each, unpadded.
+// One stage of a K/V tile in LDS: KB rows (keys) of K and of V, D*2 bytes each, unpadded.
 // Rows arrive straight from global memory with global_load_lds_dwordx4: one instruction
 // moves kRowsPerInst whole rows (lane l writes 16 bytes at M0 + 16*l), every lane with
 // its own 64-bit source address -- a fully coalesced request, no staging registers.
 //
 // Two permutations make this work with the 64 x 4-byte LDS banks:
-// * rows: instruction g of wave w fills LDS rows 16w + kRowsPerInst*g + j (j < rows per
-//   instruction), holding keys 16w + g + kInstPerWave*j, so a lane's kInstPerWave slot
-//   ids are consecutive table entries (one load) -- key_of_row() undoes it for masking;
+// * rows: instruction g of wave w fills LDS rows (KB/4)w + kRowsPerInst*g + j (j < rows
+//   per instruction), holding keys (KB/4)w + g + kInstPerWave*j, so a lane's kInstPerWave
+//   slot ids are consecutive table entries (one load) -- key_of_row() undoes it for masks;
 // * 16-byte chunks: chunk c of LDS row R sits at position c ^ swz(R), which spreads the
 //   16 rows of a K-operand ds_read_b128 phase and the 4 rows x 4 chunks of a V-operand
 //   transposing ds_read_b64 phase over distinct banks (no conflicts).
-template <int D>
+template <int D, int KB>
 struct StageLayout {
+  static_assert(KB == 32 || KB == 64, "tiles of 32 or 64 keys");
   static constexpr int kRow = D * 2;                  // bytes per row (K and V)
   static constexpr int kChunks = kRow / 16;           // 16-byte chunks per row
   static constexpr int kRowsPerInst = 64 / kChunks;   // rows one dwordx4 DMA instruction fills
-  static constexpr int kInstPerWave = kBN / 4 / kRowsPerInst;
+  static constexpr int kRowsPerWave = KB / 4;
+  static constexpr int kInstPerWave = kRowsPerWave / kRowsPerInst;
+  static_assert(kInstPerWave >= 1, "a wave's rows fill whole DMA instructions");
 };
 
-template <int D>
+template <int D, int KB>
 struct __align__(16) Stage {
-  char k[kBN * StageLayout<D>::kRow];
-  char v[kBN * StageLayout<D>::kRow];
+  char k[KB * StageLayout<D, KB>::kRow];
+  char v[KB * StageLayout<D, KB>::kRow];
 };
 
 template <int D>
@@ -84,33 +86,34 @@ __device__ __forceinline__ int swz(int R) {
   return D == 128 ? 4 * (R & 3) + ((R >> 2) & 3) : 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
 }
 
-template <int D>
+template <int D, int KB>
 __device__ __forceinline__ int key_of_row(int R) {
-  return D == 128 ? (R & ~15) | ((R & 15) >> 2) | ((R & 3) << 2) : (R & ~15) | ((R & 15) >> 3) | ((R & 7) << 1);
+  using L = StageLayout<D, KB>;
+  const int rw = R % L::kRowsPerWave;
+  return R - rw + rw / L::kRowsPerInst + L::kInstPerWave * (rw % L::kRowsPerInst);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kRowsPerWave = kBN / 4;
-
 // Slot ids for this lane's DMA rows of the tile at key0: s[g] = slot of key
 // key0 + 16w + kInstPerWave*j + g (j = lane / chunks per row).  Keys past k1 repeat the
 // slot of key k1-1 -- an in-bounds row whose scores the caller masks.
-template <int D>
+template <int D, int KB>
 struct TileSlots {
-  int s[StageLayout<D>::kInstPerWave];
+  int s[StageLayout<D, KB>::kInstPerWave];
 };
 
-template <int D>
-__device__ __forceinline__ TileSlots<D> wave_slots(const int32_t* __restrict__ trow, int key0, int k1, int wave_u,
-                                                   int lane) {
-  using L = StageLayout<D>;
-  typedef int slots_vec __attribute__((ext_vector_type(L::kInstPerWave)));
-  TileSlots<D> t;
-  const int base = key0 + wave_u * kRowsPerWave;
+template <int D, int KB>
+__device__ __forceinline__ TileSlots<D, KB> wave_slots(const int32_t* __restrict__ trow, int key0, int k1, int wave_u,
+                                                       int lane) {
+  using L = StageLayout<D, KB>;
+  TileSlots<D, KB> t;
+  const int base = key0 + wave_u * L::kRowsPerWave;
   const int k = base + L::kInstPerWave * (lane / L::kChunks);
   // one vector load per lane when every row is in range and the entries are aligned for it
-  if (base + kRowsPerWave <= k1 && (reinterpret_cast<uintptr_t>(trow + base) & (4 * L::kInstPerWave - 1)) == 0) {
+  if (L::kInstPerWave > 1 && base + L::kRowsPerWave <= k1 &&
+      (reinterpret_cast<uintptr_t>(trow + base) & (4 * L::kInstPerWave - 1)) == 0) {
+    typedef int slots_vec __attribute__((ext_vector_type(L::kInstPerWave > 1 ? L::kInstPerWave : 2)));
     const slots_vec v = *reinterpret_cast<const slots_vec*>(trow + k);
 #pragma unroll
     for (int g = 0; g < L::kInstPerWave; ++g) t.s[g] = v[g];
@@ -121,17 +124,17 @@ __device__ __forceinline__ TileSlots<D> wave_slots(const int32_t* __restrict__ t
   return t;
 }
 
-// Issue the global->LDS loads of one tile (this wave's kBN/4 rows of K and of V).
+// Issue the global->LDS loads of one tile (this wave's KB/4 rows of K and of V).
 // co[g] = this lane's byte offset within its row for instruction g (its swizzled chunk).
-template <int D>
-__device__ __forceinline__ void issue_tile(Stage<D>& dst, const char* kp, const char* vp, uint32_t row_bytes,
-                                           const TileSlots<D>& ts, const uint32_t (&co)[StageLayout<D>::kInstPerWave],
-                                           int wave_u) {
-  using L = StageLayout<D>;
+template <int D, int KB>
+__device__ __forceinline__ void issue_tile(Stage<D, KB>& dst, const char* kp, const char* vp, uint32_t row_bytes,
+                                           const TileSlots<D, KB>& ts,
+                                           const uint32_t (&co)[StageLayout<D, KB>::kInstPerWave], int wave_u) {
+  using L = StageLayout<D, KB>;
 #pragma unroll
   for (int g = 0; g < L::kInstPerWave; ++g) {
     const uint64_t off = uint64_t(uint32_t(ts.s[g])) * row_bytes + co[g];
-    const int r0 = wave_u * kRowsPerWave + g * L::kRowsPerInst;
+    const int r0 = wave_u * L::kRowsPerWave + g * L::kRowsPerInst;
     __builtin_amdgcn_global_load_lds(kp + off, (lds_ptr)(dst.k + r0 * L::kRow), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vp + off, (lds_ptr)(dst.v + r0 * L::kRow), 16, 0, 0);
   }
@@ -170,20 +173,21 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t* __r
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// One 64-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
+// One KB-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
 // visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
 // The math runs over LDS rows; the key of a row only matters for the mask.
 // c = sm_scale*log2(e); slack = kSlack / c (the same margin in raw score units).
-template <int D>
-__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, const bf16x8 (&qf)[D / 16],
+template <int D, int KB>
+__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& sm, const bf16x8 (&qf)[D / 16],
                                           int lane, bool mask, int nk, int key_pos0, int lim, float c, float slack) {
-  using L = StageLayout<D>;
+  using L = StageLayout<D, KB>;
+  constexpr int NB = KB / 32;                            // 32-key blocks of S^T
   const int r32 = lane & 31, hi = lane >> 5;
   const char* kb = sm.k + r32 * L::kRow;                 // LDS row r32 (and r32 + 32)
   const int fk = swz<D>(r32);                            // rows r32, r32 + 32 share it
-  f32x16 s[2];
+  f32x16 s[NB];
 #pragma unroll
-  for (int kb32 = 0; kb32 < 2; ++kb32) {
+  for (int kb32 = 0; kb32 < NB; ++kb32) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[kb32][j] = 0.f;
 #pragma unroll
@@ -195,16 +199,16 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   }
   if (mask) {                             // wave-uniform: only the ragged or diagonal tiles
 #pragma unroll
-    for (int kb32 = 0; kb32 < 2; ++kb32)
+    for (int kb32 = 0; kb32 < NB; ++kb32)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int t = key_of_row<D>(kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3));
+        const int t = key_of_row<D, KB>(kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3));
         if (t >= nk || key_pos0 + t > lim) s[kb32][j] = -INFINITY;
       }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb32 = 0; kb32 < 2; ++kb32)
+  for (int kb32 = 0; kb32 < NB; ++kb32)
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb32][j]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -225,7 +229,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   }
   const float mc = (ws.m == -INFINITY ? 0.f : ws.m) * c;
 #pragma unroll
-  for (int kb32 = 0; kb32 < 2; ++kb32)
+  for (int kb32 = 0; kb32 < NB; ++kb32)
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[kb32][j] = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
   // V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
@@ -243,7 +247,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D>& sm, 
   const char* vb0 = sm.v + vr0 * L::kRow + 8 * (i16 & 1);
   const char* vb1 = vb0 + 8 * L::kRow;
 #pragma unroll
-  for (int kstep = 0; kstep < 4; ++kstep) {
+  for (int kstep = 0; kstep < KB / 16; ++kstep) {
     const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
     uint4 pu;
     pu.x = pack_bf16(s[kb32][h8 + 0], s[kb32][h8 + 1]);
@@ -287,28 +291,28 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // t-1 used); it then issues the slot ids of tile t+NS and the loads of tile t+NS-1 into
 // that stage, and computes tile t.  While tile t+1 is in flight the wait leaves exactly
 // the loads issued after tile t's (one iteration's worth) outstanding.
-template <int D>
+template <int D, int KB>
 struct StreamArgs {
   const char* kc;
   const char* vc;
   const int32_t* trow;
   uint32_t row_bytes;
-  uint32_t co[StageLayout<D>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
+  uint32_t co[StageLayout<D, KB>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
   int k0, k1, ntiles, mask_from, lim, wave_u, lane;
   float c, slack;
   bool has_rows;
 };
 
 // Iteration t of the pipeline; its tile sits in stage t % NS.
-template <int D, int NS, bool SKIP_EMPTY>
-__device__ __forceinline__ void stream_step(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
-                                            const StreamArgs<D>& a, TileSlots<D>& s_next, int t) {
-  using L = StageLayout<D>;
+template <int D, int KB, int NS, bool SKIP_EMPTY>
+__device__ __forceinline__ void stream_step(WaveState<D>& ws, Stage<D, KB> (&sm)[NS], const bf16x8 (&qf)[D / 16],
+                                            const StreamArgs<D, KB>& a, TileSlots<D, KB>& s_next, int t) {
+  using L = StageLayout<D, KB>;
   // K + V DMA and the next slot loads (one vector load, or kInstPerWave single loads):
   // at least this many per iteration
   constexpr int kPerIter = 2 * L::kInstPerWave + 1;
-  const int key0 = a.k0 + t * kBN;
-  const int nk = min(kBN, a.k1 - key0);
+  const int key0 = a.k0 + t * KB;
+  const int nk = min(KB, a.k1 - key0);
   // After tile t's loads came, in order: the next tiles' (issued one iteration each, at
   // least kPerIter instructions per iteration) -- exactly when all of them exist.
   // (vmcnt counts to 63: a smaller count only waits a little longer)
@@ -316,24 +320,24 @@ __device__ __forceinline__ void stream_step(WaveState<D>& ws, Stage<D> (&sm)[NS]
   if (NS > 2 && t + NS - 2 < a.ntiles && t >= NS - 2) wait_vmcnt_barrier<kAfter>();
   else wait_vmcnt_barrier<0>();
   if (t + NS - 1 < a.ntiles) {
-    issue_tile<D>(sm[(t + NS - 1) % NS], a.kc, a.vc, a.row_bytes, s_next, a.co, a.wave_u);
-    s_next = wave_slots<D>(a.trow, a.k0 + (t + NS) * kBN, a.k1, a.wave_u, a.lane);
+    issue_tile<D, KB>(sm[(t + NS - 1) % NS], a.kc, a.vc, a.row_bytes, s_next, a.co, a.wave_u);
+    s_next = wave_slots<D, KB>(a.trow, a.k0 + (t + NS) * KB, a.k1, a.wave_u, a.lane);
   }
   if (!SKIP_EMPTY || a.has_rows) {
-    const bool mask = nk < kBN || key0 + kBN > a.mask_from;
-    wave_tile<D>(ws, sm[t % NS], qf, a.lane, mask, nk, key0, a.lim, a.c, a.slack);
+    const bool mask = nk < KB || key0 + KB > a.mask_from;
+    wave_tile<D, KB>(ws, sm[t % NS], qf, a.lane, mask, nk, key0, a.lim, a.c, a.slack);
   }
 }
 
 
-template <int D, int NS, bool SKIP_EMPTY>
-__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS], const bf16x8 (&qf)[D / 16],
+template <int D, int KB, int NS, bool SKIP_EMPTY>
+__device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)[NS], const bf16x8 (&qf)[D / 16],
                                             const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                                             const int32_t* __restrict__ trow, int Hkv, int k0, int k1,
                                             int mask_from, int lim, float c, bool has_rows, int tid) {
   if (k0 >= k1) return;
-  using L = StageLayout<D>;
-  StreamArgs<D> a;
+  using L = StageLayout<D, KB>;
+  StreamArgs<D, KB> a;
   a.kc = reinterpret_cast<const char*>(kp);
   a.vc = reinterpret_cast<const char*>(vp);
   a.trow = trow;
@@ -344,10 +348,11 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS]
   // that belongs at its LDS position (the swizzle depends on the LDS row mod 16)
 #pragma unroll
   for (int g = 0; g < L::kInstPerWave; ++g)
-    a.co[g] = 16u * uint32_t((a.lane % L::kChunks) ^ swz<D>(g * L::kRowsPerInst + a.lane / L::kChunks));
+    a.co[g] = 16u * uint32_t((a.lane % L::kChunks) ^
+                             swz<D>(a.wave_u * L::kRowsPerWave + g * L::kRowsPerInst + a.lane / L::kChunks));
   a.k0 = k0;
   a.k1 = k1;
-  a.ntiles = (k1 - k0 + kBN - 1) / kBN;
+  a.ntiles = (k1 - k0 + KB - 1) / KB;
   a.mask_from = mask_from;
   a.lim = lim;
   a.c = c;
@@ -356,20 +361,22 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D> (&sm)[NS]
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (j < a.ntiles)
-      issue_tile<D>(sm[j], a.kc, a.vc, a.row_bytes, wave_slots<D>(trow, k0 + j * kBN, k1, a.wave_u, a.lane), a.co,
-                    a.wave_u);
-  TileSlots<D> s_next = wave_slots<D>(trow, k0 + (NS - 1) * kBN, k1, a.wave_u, a.lane);
-  for (int t = 0; t < a.ntiles; ++t) stream_step<D, NS, SKIP_EMPTY>(ws, sm, qf, a, s_next, t);
+      issue_tile<D, KB>(sm[j], a.kc, a.vc, a.row_bytes, wave_slots<D, KB>(trow, k0 + j * KB, k1, a.wave_u, a.lane),
+                        a.co, a.wave_u);
+  TileSlots<D, KB> s_next = wave_slots<D, KB>(trow, k0 + (NS - 1) * KB, k1, a.wave_u, a.lane);
+  for (int t = 0; t < a.ntiles; ++t) stream_step<D, KB, NS, SKIP_EMPTY>(ws, sm, qf, a, s_next, t);
 }
 
 // ------------------------------------------------------------------ extend (bf16)
+// Extend: 64-key tiles, two stages (2 x 32 KiB at d128; two workgroups per CU).
+constexpr int kExtKB = 64, kExtNS = 2;
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
     int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out) {
-  __shared__ Stage<D> sm[2];
+  __shared__ Stage<D, kExtKB> sm[kExtNS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
   const int tpb = 128 / G;                        // tokens per tile
@@ -397,7 +404,7 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
   const int mask_from = prefix + t0 + 1;          // keys below this are visible to every row
   const bool has_rows = wave * 32 < ntok * G;
   const float c = sm_scale * kLog2e;
-  stream_keys<D, 2, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
+  stream_keys<D, kExtKB, kExtNS, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
                  Hkv, 0, key_end, mask_from, lim, c, has_rows, tid);
   if (!valid) return;
   float l = ws.l + __shfl_xor(ws.l, 32);
@@ -417,6 +424,8 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
 }
 
 // ------------------------------------------------------------------ decode (bf16)
+// Decode: 64-key tiles, two stages, two workgroups per CU (as extend).
+constexpr int kDecKB = 64, kDecNS = 2;
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kpool;
@@ -463,7 +472,7 @@ __device__ __forceinline__ PartList part_list(const DecodeArgs& a, int b) {
 // item writes one partial (o / l, lse) per (request, head) for decode_merge_kernel.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) {
-  __shared__ Stage<D> sm[2];
+  __shared__ Stage<D, kDecKB> sm[kDecNS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.Hq / a.Hkv;
   const int kvh = blockIdx.x % a.Hkv;
@@ -490,7 +499,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   WaveState<D> ws;
   wave_init<D>(ws);
   const bool has_rows = wave * 32 < nreq * G;
-  stream_keys<D, 2, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
+  stream_keys<D, kDecKB, kDecNS, true>(ws, sm, qf, a.kpool + int64_t(kvh) * D, a.vpool + int64_t(kvh) * D,
                  a.req_to_token + int64_t(rep) * a.ld, a.Hkv, k0, k1, k1, INT32_MAX,
                  a.sm_scale * kLog2e, has_rows, tid);
   if (!valid) return;

@@ -161,6 +161,20 @@ int rs_decode_plan_build(const rs_tree* t, const int64_t* nodes, const int32_t* 
     if (P >= (int64_t(1) << 31) / (int64_t(G) * D * Hkv))
       return rs::fail(RS_E_UNSUPPORTED, "rs_decode_plan_build: batch too large for one plan");
 
+    // the longest items first (their keys are the memory traffic), so that no long item
+    // starts late and runs on an otherwise idle chip; items are independent
+    {
+      std::vector<int32_t> ord(n_items);
+      for (int32_t i = 0; i < n_items; ++i) ord[i] = i;
+      auto keys_of = [&](int32_t i) { return items[size_t(i) * rs::kItemWords + 1] - items[size_t(i) * rs::kItemWords]; };
+      std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return keys_of(x) > keys_of(y); });
+      std::vector<int32_t> sorted(items.size());
+      for (int32_t i = 0; i < n_items; ++i)
+        std::copy_n(items.begin() + size_t(ord[i]) * rs::kItemWords, rs::kItemWords,
+                    sorted.begin() + size_t(i) * rs::kItemWords);
+      items.swap(sorted);
+    }
+
     // 5. device image
     auto p = std::make_unique<rs_plan>();
     std::vector<int32_t>& img = p->image;
