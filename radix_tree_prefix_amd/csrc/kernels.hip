@@ -173,48 +173,72 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t* __r
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// One KB-key tile for one wave.  nk = valid keys in the tile; a key at tile index t is
-// visible iff t < nk and key_pos0 + t <= lim (lim = the row's last visible position).
-// The math runs over LDS rows; the key of a row only matters for the mask.
+// The steps of one KB-key tile for one wave (the math runs over LDS rows; the key of a
+// row only matters for the mask):
+//   qk:          S^T = K . Q^T                      (MFMA, K from LDS)
+//   mask_scores: -inf where key >= nk or key_pos0 + key > lim (lim = the row's last
+//                visible position)
+//   row_max:     max over the tile of each query row (both lane halves)
+//   update_ref:  move the reference point of the exponentials if needed (rescales O, l)
+//   weights:     P^T = exp2(S*c - m*c) packed to bf16, and the row sums of those weights
+//   pv:          O^T += V^T . P^T                   (MFMA, V^T from LDS)
 // c = sm_scale*log2(e); slack = kSlack / c (the same margin in raw score units).
+template <int KB>
+struct Scores {
+  f32x16 s[KB / 32];
+};
+
+template <int KB>
+struct Weights {
+  uint4 p[KB / 16];       // P^T in bf16 pairs, one B operand per 16 keys
+};
+
 template <int D, int KB>
-__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& sm, const bf16x8 (&qf)[D / 16],
-                                          int lane, bool mask, int nk, int key_pos0, int lim, float c, float slack) {
+__device__ __forceinline__ void qk(Scores<KB>& sc, const Stage<D, KB>& sm, const bf16x8 (&qf)[D / 16], int lane) {
   using L = StageLayout<D, KB>;
-  constexpr int NB = KB / 32;                            // 32-key blocks of S^T
   const int r32 = lane & 31, hi = lane >> 5;
   const char* kb = sm.k + r32 * L::kRow;                 // LDS row r32 (and r32 + 32)
   const int fk = swz<D>(r32);                            // rows r32, r32 + 32 share it
-  f32x16 s[NB];
 #pragma unroll
-  for (int kb32 = 0; kb32 < NB; ++kb32) {
+  for (int kb32 = 0; kb32 < KB / 32; ++kb32) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[kb32][j] = 0.f;
+    for (int j = 0; j < 16; ++j) sc.s[kb32][j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       // elements 16ks + 8hi .. +8 of the row = 16-byte chunk 2ks + hi
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + kb32 * 32 * L::kRow + 16 * ((2 * ks + hi) ^ fk));
-      s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb32], 0, 0, 0);
+      sc.s[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc.s[kb32], 0, 0, 0);
     }
   }
-  if (mask) {                             // wave-uniform: only the ragged or diagonal tiles
+}
+
+template <int D, int KB>
+__device__ __forceinline__ void mask_scores(Scores<KB>& sc, int lane, int nk, int key_pos0, int lim) {
+  const int hi = lane >> 5;
 #pragma unroll
-    for (int kb32 = 0; kb32 < NB; ++kb32)
+  for (int kb32 = 0; kb32 < KB / 32; ++kb32)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = key_of_row<D, KB>(kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3));
-        if (t >= nk || key_pos0 + t > lim) s[kb32][j] = -INFINITY;
-      }
-  }
+    for (int j = 0; j < 16; ++j) {
+      const int t = key_of_row<D, KB>(kb32 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3));
+      if (t >= nk || key_pos0 + t > lim) sc.s[kb32][j] = -INFINITY;
+    }
+}
+
+template <int KB>
+__device__ __forceinline__ float row_max(const Scores<KB>& sc) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb32 = 0; kb32 < NB; ++kb32)
+  for (int kb32 = 0; kb32 < KB / 32; ++kb32)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb32][j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // The reference point m of the exponentials moves only when some row's maximum
-  // exceeds it by more than kSlack (in exp2 units), so weights stay below 2^kSlack and
-  // most tiles skip the rescale of O and l; softmax does not depend on the point.
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc.s[kb32][j]);
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// The reference point m of the exponentials moves only when some row's maximum exceeds
+// it by more than kSlack (in exp2 units), so weights stay below 2^kSlack and most tiles
+// skip the rescale of O and l; softmax does not depend on the point.
+template <int D>
+__device__ __forceinline__ void update_ref(WaveState<D>& ws, float mx, float c, float slack) {
   if (__builtin_amdgcn_ballot_w64(mx > ws.m + slack)) {
     const float m_new = fmaxf(ws.m, mx);
     const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -227,18 +251,41 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& 
       for (int j = 0; j < 16; ++j) ws.o[mb][j] *= alpha;
     ws.m = m_new;
   }
-  const float mc = (ws.m == -INFINITY ? 0.f : ws.m) * c;
-#pragma unroll
-  for (int kb32 = 0; kb32 < NB; ++kb32)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[kb32][j] = __builtin_amdgcn_exp2f(fmaf(s[kb32][j], c, -mc));
-  // V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
-  // element i%4 of the 8-byte pieces read by lanes i/4 + 4k (k = 0..3).  Provider lane j
-  // reads row rbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
-  // V[rbase + k][dbase + i], k = 0..3: the four rows of its P^T slots 4r..4r+3.
+}
+
+__device__ __forceinline__ float ref_times_c(float m, float c) { return (m == -INFINITY ? 0.f : m) * c; }
+
+// Returns this lane's half of the row sum of the weights as the second MFMA sees them (bf16).
+template <int KB>
+__device__ __forceinline__ float weights(Weights<KB>& w, const Scores<KB>& sc, float c, float mc) {
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
   float sum = 0.f;
-  const int i16 = lane & 15, gpar = (lane >> 4) & 1;
+#pragma unroll
+  for (int kstep = 0; kstep < KB / 16; ++kstep) {
+    const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(sc.s[kb32][h8 + i], c, -mc));
+    w.p[kstep].x = pack_bf16(e[0], e[1]);
+    w.p[kstep].y = pack_bf16(e[2], e[3]);
+    w.p[kstep].z = pack_bf16(e[4], e[5]);
+    w.p[kstep].w = pack_bf16(e[6], e[7]);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.p[kstep].x), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.p[kstep].y), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.p[kstep].z), kOnes, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.p[kstep].w), kOnes, sum, false);
+  }
+  return sum;
+}
+
+// V^T operand by transposing LDS reads: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte pieces read by lanes i/4 + 4k (k = 0..3).  Provider lane j
+// reads row rbase + j/4 at d = dbase + 4*(j%4), so receiver lane i gets
+// V[rbase + k][dbase + i], k = 0..3: the four rows of its P^T slots 4r..4r+3.
+template <int D, int KB>
+__device__ __forceinline__ void pv(WaveState<D>& ws, const Stage<D, KB>& sm, const Weights<KB>& w, int lane) {
+  using L = StageLayout<D, KB>;
+  const int hi = lane >> 5, i16 = lane & 15, gpar = (lane >> 4) & 1;
   // this lane's rows hi*4 + i16/4 (+8, +16*kstep) at bytes 32gpar + 8(i16%4) + 64mb:
   // chunk 2gpar + (i16%4)/2 + 4mb, half i16%2; the swizzle depends on the row mod 16
   const int vr0 = hi * 4 + (i16 >> 2);
@@ -248,18 +295,7 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& 
   const char* vb1 = vb0 + 8 * L::kRow;
 #pragma unroll
   for (int kstep = 0; kstep < KB / 16; ++kstep) {
-    const int kb32 = kstep >> 1, h8 = (kstep & 1) * 8;
-    uint4 pu;
-    pu.x = pack_bf16(s[kb32][h8 + 0], s[kb32][h8 + 1]);
-    pu.y = pack_bf16(s[kb32][h8 + 2], s[kb32][h8 + 3]);
-    pu.z = pack_bf16(s[kb32][h8 + 4], s[kb32][h8 + 5]);
-    pu.w = pack_bf16(s[kb32][h8 + 6], s[kb32][h8 + 7]);
-    const bf16x8 b = __builtin_bit_cast(bf16x8, pu);
-    // the row sum of the weights as the second MFMA sees them (bf16), two per dot2
-    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.x), kOnes, sum, false);
-    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.y), kOnes, sum, false);
-    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.z), kOnes, sum, false);
-    sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu.w), kOnes, sum, false);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, w.p[kstep]);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       const char* p0 = vb0 + kstep * 16 * L::kRow + 16 * ((cv + 4 * mb) ^ fv0);
@@ -271,6 +307,19 @@ __device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& 
       ws.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ws.o[mb], 0, 0, 0);
     }
   }
+}
+
+// All steps of one tile in order.
+template <int D, int KB>
+__device__ __forceinline__ void wave_tile(WaveState<D>& ws, const Stage<D, KB>& sm, const bf16x8 (&qf)[D / 16],
+                                          int lane, bool mask, int nk, int key_pos0, int lim, float c, float slack) {
+  Scores<KB> sc;
+  qk<D, KB>(sc, sm, qf, lane);
+  if (mask) mask_scores<D, KB>(sc, lane, nk, key_pos0, lim);   // wave-uniform: ragged or diagonal tiles
+  update_ref<D>(ws, row_max<KB>(sc), c, slack);
+  Weights<KB> w;
+  const float sum = weights<KB>(w, sc, c, ref_times_c(ws.m, c));
+  pv<D, KB>(ws, sm, w, lane);
   ws.l += sum;
 }
 
