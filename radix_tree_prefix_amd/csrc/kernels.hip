@@ -8,18 +8,19 @@
 // the unmatched suffix is prefilled attending to the reused KV as if it had just
 // been computed).
 //
-// bf16 tile engine (extend and decode share it).  A workgroup is 4 waves; each wave
-// owns up to 32 query rows (rows = tokens x heads of one KV-head group in extend,
-// requests x heads in decode).  Per 64-key tile the workgroup gathers the K rows
-// (row-major) and the V rows (transposed, keys permuted) through the index table
-// into LDS, then each wave runs, on 32x32x16 bf16 MFMAs:
-//     S^T[key][row] = K[key][:] . Q[row][:]      (A = K from LDS, B = Q^T in VGPRs)
-//     O^T[d][row]  += V^T[d][key] . P^T[key][row] (A = V^T from LDS, B = P^T in VGPRs)
-// With S^T in the accumulator a lane holds 32 scores of one query row (its partner
-// lane l^32 holds the other 32), so the online-softmax max/sum/rescale is lane-local
-// plus one cross-half exchange, and P^T feeds the second MFMA from the same registers
-// with no shuffle: the permuted key order of V^T in LDS matches the accumulator
-// layout.  fp32 runs a VALU path (one wave per query row).
+// bf16 attention runs on two MFMA tile engines with one operand scheme.  K and V rows are
+// gathered through the index table into LDS tiles; per tile, on 32x32x16 bf16 MFMAs:
+//     S^T[key][row] = K[key][:] . Q[row][:]      (A = K from LDS, B = Q^T in registers)
+//     O^T[d][row]  += V^T[d][key] . P^T[key][row] (A = V^T from LDS, B = P^T in registers)
+// With S^T in the accumulator a lane holds the scores of one query row for half the
+// keys (its partner lane l^32 holds the other half), so softmax bookkeeping is
+// lane-local plus one cross-half exchange, and P^T feeds the second MFMA from the same
+// registers: the key order that transposing LDS reads give V^T matches the accumulator.
+// * decode: 4 waves of 32 rows (requests x heads), 64-key tiles, online softmax with a
+//   lazily moved reference point;
+// * extend: 4 waves of 64 rows (tokens x heads) in two row blocks, 32-key tiles, a
+//   software-pipelined loop and a per-row reference fixed from the first tile.
+// fp32 runs a VALU path (one wave per query row).
 
 #include <hip/hip_runtime.h>
 
@@ -417,18 +418,385 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 }
 
 // ------------------------------------------------------------------ extend (bf16)
-// Extend: 64-key tiles, two stages (2 x 32 KiB at d128; two workgroups per CU).
-constexpr int kExtKB = 64, kExtNS = 2;
+// Extend engine.  Each wave owns 64 query rows as two 32-row blocks, and every K and V
+// operand it reads from LDS feeds the MFMAs of both blocks, so LDS reads per flop are
+// half those of a 32-row wave.  A workgroup is 4 waves (256 rows) and a CU holds one: each
+// wave has a SIMD and up to 512 registers to itself.  The Q fragments and the O
+// accumulators stay in AGPRs (only MFMAs touch them in the loop); the scores, weights and
+// addresses use the VGPRs.
+//
+// Tiles of 32 keys stream through kExtNS LDS stages, kExtNS - 2 tiles ahead of the math.
+// Their slot ids reach LDS the same way (a small ring filled one DMA per wave per tile,
+// further ahead still), so every load in the loop goes global -> LDS and the waits count
+// exactly.
+//
+// The loop is software-pipelined by one tile so that one wave overlaps its own matrix
+// and vector work.  Iteration t: S(t) = K(t) Q^T runs on the matrix cores while the VALU
+// turns S(t-1) into weights; then O += V(t-1)^T P(t-1); then S(t) moves from the MFMA
+// result registers to VGPRs (the copy is the pipeline's buffer swap) and, on the causal
+// diagonal or a ragged end, is masked.
+//
+// Softmax reference.  Each row's reference point is the maximum of its scores in tile 0
+// and stays fixed for the pass, so the loop never rescales O.  Later scores may exceed it:
+// weights up to 2^kExtGuard are exact in fp32 and bf16.  A lane that sees a larger excess
+// raises a guard flag, and if any lane of the workgroup did, a second pass recomputes the
+// rows with each row's true maximum as the reference (every weight <= 1).  Softmax does
+// not depend on the reference point.
+constexpr int kExtKB = 32;           // keys per tile
+constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
+constexpr int kExtRows = 256;        // query rows per workgroup: 4 waves x 64
+constexpr int kExtWaves = kExtRows / 64;
+constexpr int kExtAhead = kExtNS - 2;            // tiles in flight ahead of the math
+constexpr int kExtSlotLead = 2 * kExtAhead + 1;  // slot ids are loaded this many tiles ahead
+constexpr int kExtRing = 16;                     // slot-id ring entries (tiles)
+static_assert(kExtRing >= kExtSlotLead && kExtRing > kExtAhead, "slot ring too small");
+constexpr float kExtGuard = 64.f;    // first-pass weights stay below 2^kExtGuard
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
+struct ExtState {
+  f32x16 o[2][D / 32];          // O^T per row block (layout as WaveState)
+  float mc[2];                  // reference point times c, per row block (fixed per pass)
+  float lim[2];                 // guard: raw scores above this would weigh over 2^kExtGuard
+  float mx[2];                  // this lane's running maximum of raw scores
+  float l[2];                   // this lane's halves of the running sums
+  bool guard;
+};
+
+struct Weights2 {
+  uint4 p[2][kExtKB / 16];      // [row block][16-key step]: P^T in bf16 pairs
+};
+
+// Per-lane LDS byte offsets of the MFMA operands within a stage: K chunk of step ks for
+// row r32, and the two transposing-read pieces of V for output block mb.  The swizzle is
+// fixed per lane, so these are computed once.
+template <int D>
+struct ExtOffsets {
+  uint32_t k[D / 16];
+  uint32_t v0[D / 32], v1[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ ExtOffsets<D> ext_offsets(int lane) {
+  using L = StageLayout<D, kExtKB>;
+  ExtOffsets<D> off;
+  const int r32 = lane & 31, hi = lane >> 5, i16 = lane & 15, gpar = (lane >> 4) & 1;
+  const int fk = swz<D>(r32);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) off.k[ks] = r32 * L::kRow + 16 * ((2 * ks + hi) ^ fk);
+  const int vr0 = hi * 4 + (i16 >> 2), cv = 2 * gpar + ((i16 & 3) >> 1);
+  const int fv0 = swz<D>(vr0), fv1 = swz<D>(vr0 + 8);
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    off.v0[mb] = vr0 * L::kRow + 8 * (i16 & 1) + 16 * ((cv + 4 * mb) ^ fv0);
+    off.v1[mb] = (vr0 + 8) * L::kRow + 8 * (i16 & 1) + 16 * ((cv + 4 * mb) ^ fv1);
+  }
+  return off;
+}
+
+// K fragments of one tile (A operands of S^T = K Q^T), read once for both row blocks.
+template <int D>
+struct KFrags {
+  bf16x8 a[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ KFrags<D> ext_read_k(const char* kst, const ExtOffsets<D>& off) {
+  KFrags<D> f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) f.a[ks] = *reinterpret_cast<const bf16x8*>(kst + off.k[ks]);
+  return f;
+}
+
+// S^T of both row blocks (results in the MFMA's accumulation registers).
+template <int D>
+__device__ __forceinline__ void ext_qk(f32x16 (&sc)[2], const KFrags<D>& kf, const bf16x8 (&qf)[2][D / 16]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sc[rb][j] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[ks], qf[rb][ks], sc[rb], 0, 0, 0);
+}
+
+// Key index within the tile of score element j (lane half 0; half 1 adds 4).
+__device__ __forceinline__ constexpr int ext_key(int j) { return 8 * (j >> 2) + (j & 3); }
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, v[j]);
+  return m;
+}
+
+// Weights P = bf16(exp2(S*c - m*c)) of both row blocks, their row sums (of the bf16
+// weights, as the second MFMA sees them), the running maxima and the guard.
+template <int D>
+__device__ __forceinline__ void ext_weights(Weights2& w, ExtState<D>& es, const f32x16 (&sc)[2], float c) {
+  const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float tmax = max16(sc[rb]);
+    es.mx[rb] = fmaxf(es.mx[rb], tmax);
+    es.guard |= tmax > es.lim[rb];
+    float sum = 0.f;
+#pragma unroll
+    for (int kstep = 0; kstep < kExtKB / 16; ++kstep) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * kstep + i], c, -es.mc[rb]));
+      uint4& p = w.p[rb][kstep];
+      p.x = pack_bf16(e[0], e[1]);
+      p.y = pack_bf16(e[2], e[3]);
+      p.z = pack_bf16(e[4], e[5]);
+      p.w = pack_bf16(e[6], e[7]);
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.x), kOnes, sum, false);
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.y), kOnes, sum, false);
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.z), kOnes, sum, false);
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p.w), kOnes, sum, false);
+    }
+    es.l[rb] += sum;
+  }
+}
+
+// V^T fragments of one tile (A operands of O^T += V^T P^T), by transposing LDS reads.
+template <int D>
+struct VFrags {
+  bf16x8 a[kExtKB / 16][D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ VFrags<D> ext_read_v(const char* vst, const ExtOffsets<D>& off) {
+  using L = StageLayout<D, kExtKB>;
+  VFrags<D> f;
+#pragma unroll
+  for (int kstep = 0; kstep < kExtKB / 16; ++kstep)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      const char* p0 = vst + off.v0[mb] + kstep * 16 * L::kRow;
+      const char* p1 = vst + off.v1[mb] + kstep * 16 * L::kRow;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      f.a[kstep][mb] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+          lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]});
+    }
+  return f;
+}
+
+// O^T += V^T P^T for both row blocks.
+template <int D>
+__device__ __forceinline__ void ext_pv(ExtState<D>& es, const VFrags<D>& vf, const Weights2& w) {
+#pragma unroll
+  for (int kstep = 0; kstep < kExtKB / 16; ++kstep)
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        es.o[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.a[kstep][mb], __builtin_bit_cast(bf16x8, w.p[rb][kstep]),
+                                                               es.o[rb][mb], 0, 0, 0);
+}
+
+template <int D>
+struct ExtStream {
+  const char* kc;             // K pool at this KV head
+  const char* vc;
+  const int32_t* trow;        // index-table row
+  uint32_t row_bytes;
+  uint32_t co[StageLayout<D, kExtKB>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
+  int k1, ntiles, mask_from, wave_u, lane;
+  int jrow;                   // this lane's row within a DMA instruction
+  int hik;                    // 4 in the upper lane half: its score elements sit 4 keys later
+  int lim[2];                 // last visible key position of this lane's row per block (-1: none)
+  float c;
+};
+
+// LDS of the extend workgroup: the K/V stages and the slot-id ring.
+template <int D>
+struct ExtShared {
+  Stage<D, kExtKB> st[kExtNS];
+  int32_t ring[kExtRing][kExtWaves][64];   // per tile and wave: its 8 slot ids, repeated
+};
+
+// Global -> LDS loads issued through inline assembly.  The LDS address goes through M0,
+// set in the same statement.  The compiler does not see these as LDS writes, so it adds
+// no waits of its own before later LDS reads (it would wait for every load in flight);
+// each wait on them is explicit instead: the loop's vmcnt wait and barrier.  Nor do they
+// clobber memory: the LDS they write is read only after a later wait-and-barrier
+// statement, which orders every memory access, so LDS reads may move around them.
+// (M0 is a reserved register: the compiler warns about it in a clobber list, yet nothing
+// else in the extend kernel reads M0, and the clobber keeps it from assuming otherwise.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((__attribute__((address_space(3))) const void*)(p)));
+}
+
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {   // lane l -> lds + 16*l
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+}
+
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {    // lane l -> lds + 4*l
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "m0");
+}
+#pragma clang diagnostic pop
+
+// Slot ids of tile x into this wave's ring row: lane l loads the id of key 8*wave + l%8
+// (a full-wave load, no branch); keys past k1 repeat the last slot.
+template <int D>
+__device__ __forceinline__ void ext_slot_dma(ExtShared<D>& sh, const ExtStream<D>& a, int x) {
+  constexpr int kPerWave = kExtKB / kExtWaves;
+  const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * kPerWave + (a.lane % kPerWave), a.k1 - 1);
+  dma_b32(src, lds_addr(&sh.ring[x % kExtRing][a.wave_u][0]));
+}
+
+// This lane's slot id for each of its DMA instructions of tile x, from the ring.
+template <int D>
+struct ExtRowSlots {
+  int s[StageLayout<D, kExtKB>::kInstPerWave];
+};
+
+template <int D>
+__device__ __forceinline__ ExtRowSlots<D> ext_read_slots(const ExtShared<D>& sh, const ExtStream<D>& a, int x) {
+  using L = StageLayout<D, kExtKB>;
+  ExtRowSlots<D> r;
+#pragma unroll
+  for (int g = 0; g < L::kInstPerWave; ++g) r.s[g] = sh.ring[x % kExtRing][a.wave_u][g * L::kRowsPerInst + a.jrow];
+  return r;
+}
+
+// Global -> LDS loads of this wave's K and V rows of one tile.
+template <int D>
+__device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStream<D>& a, const ExtRowSlots<D>& sl) {
+  using L = StageLayout<D, kExtKB>;
+#pragma unroll
+  for (int g = 0; g < L::kInstPerWave; ++g) {
+    const uint64_t off = uint64_t(uint32_t(sl.s[g])) * a.row_bytes + a.co[g];
+    const int r0 = a.wave_u * L::kRowsPerWave + g * L::kRowsPerInst;
+    dma_b128(a.kc + off, lds_addr(dst.k + r0 * L::kRow));
+    dma_b128(a.vc + off, lds_addr(dst.v + r0 * L::kRow));
+  }
+}
+
+// Wait until tile t has landed for the whole workgroup (this wave's loads, then a
+// barrier).  Every iteration issues, in this order or not, one slot-id load and the tile
+// kExtAhead ahead (2*kInstPerWave loads; past the last tile they reload its last row into
+// a stage nobody reads), and loads complete in issue order: after tile t's loads come
+// those of the kExtAhead - 1 iterations since, so at most kAfter may stay outstanding.
+// Tiles issued before the loop wait for all.
+template <int D>
+__device__ __forceinline__ void ext_wait(int t) {
+  constexpr int kAfter = (kExtAhead - 1) * (1 + 2 * StageLayout<D, kExtKB>::kInstPerWave);
+  static_assert(kAfter < 64, "vmcnt is 6 bits");
+  if (t >= kExtAhead) wait_vmcnt_barrier<kAfter>();
+  else wait_vmcnt_barrier<0>();
+}
+
+// Scores of tile t to VGPRs (the next iteration's operand) and, for MASK, -inf past this
+// lane's last visible key or the tile's last key.
+template <int D, bool MASK>
+__device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (&src)[2], const ExtStream<D>& a, int t) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    dst[rb] = src[rb];
+    asm volatile("" : "+v"(dst[rb]));
+  }
+  if (MASK) {
+    const int key0 = t * kExtKB;
+    const int nk = min(kExtKB, a.k1 - key0);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int thr = min(a.lim[rb] - key0, nk - 1) - a.hik;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (ext_key(j) > thr) dst[rb][j] = -INFINITY;
+    }
+  }
+}
+
+// Iterations [t_begin, t_end), t_begin >= 1: sprev holds S(t-1) in VGPRs on entry and
+// S(t_end-1) on exit.
+template <int D, bool MASK>
+__device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
+                                          const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[2],
+                                          int t_begin, int t_end) {
+  for (int t = t_begin; t < t_end; ++t) {
+    ext_wait<D>(t);
+    const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, t + kExtAhead);
+    const KFrags<D> kf = ext_read_k<D>(sh.st[t % kExtNS].k, off);
+    const VFrags<D> vf = ext_read_v<D>(sh.st[(t - 1) % kExtNS].v, off);
+    ext_slot_dma<D>(sh, a, t + kExtSlotLead);
+    ext_kv_dma<D>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
+    f32x16 scur[2];
+    ext_qk<D>(scur, kf, qf);
+    Weights2 w;
+    ext_weights<D>(w, es, sprev, a.c);
+    ext_pv<D>(es, vf, w);
+    ext_take_scores<D, MASK>(sprev, scur, a, t);
+    __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
+  }
+}
+
+// One pass over keys [0, k1).  first_pass: the references come from tile 0's row maxima;
+// otherwise es.mc is already set.
+template <int D>
+__device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
+                                         const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, bool first_pass) {
+  // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
+  const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
+  // prologue: slot ids of the first tiles, then their K/V
+  for (int x = 0; x < kExtSlotLead; ++x) ext_slot_dma<D>(sh, a, x);
+  wait_vmcnt_barrier<0>();
+  for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D>(sh.st[x], a, ext_read_slots<D>(sh, a, x));
+  // tile 0: its scores only
+  ext_wait<D>(0);
+  ext_slot_dma<D>(sh, a, kExtSlotLead);
+  f32x16 sprev[2];
+  {
+    const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, kExtAhead);
+    const KFrags<D> kf = ext_read_k<D>(sh.st[0].k, off);
+    ext_kv_dma<D>(sh.st[kExtAhead % kExtNS], a, sl);
+    f32x16 scur[2];
+    ext_qk<D>(scur, kf, qf);
+    if (t_mask == 0) ext_take_scores<D, true>(sprev, scur, a, 0);
+    else ext_take_scores<D, false>(sprev, scur, a, 0);
+  }
+  if (first_pass) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float m = max16(sprev[rb]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float m_ref = (m == -INFINITY) ? 0.f : m;
+      es.mc[rb] = m_ref * a.c;
+      es.lim[rb] = m_ref + kExtGuard / a.c;
+    }
+  }
+  const int t_split = max(1, t_mask);
+  ext_iters<D, false>(es, sh, off, qf, a, sprev, 1, t_split);
+  ext_iters<D, true>(es, sh, off, qf, a, sprev, t_split, a.ntiles);
+  // the last tile's weights and P.V
+  Weights2 w;
+  ext_weights<D>(w, es, sprev, a.c);
+  ext_pv<D>(es, ext_read_v<D>(sh.st[(a.ntiles - 1) % kExtNS].v, off), w);
+  // the loads past the last tile have landed, and every wave is done with the stages and
+  // the ring, before a later pass refills them or the workgroup ends
+  wait_vmcnt_barrier<0>();
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
     int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out) {
-  __shared__ Stage<D, kExtKB> sm[kExtNS];
+  static_assert(kThreads == 64 * kExtWaves, "one wave per 64 rows");
+  __shared__ ExtShared<D> sh;
+  using L = StageLayout<D, kExtKB>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
-  const int tpb = 128 / G;                        // tokens per tile
+  const int tpb = kExtRows / G;                   // tokens per tile
   const int kvh = blockIdx.x % Hkv;
   const int rest = blockIdx.x / Hkv;
   // requests in the given order; within a request the later (longer) q-tiles first
@@ -440,36 +808,90 @@ __global__ void __launch_bounds__(kThreads, 2) extend_bf16_kernel(
   const int prefix = prefix_lens[b];
   const int qo = qo_indptr[b];
   const int ntok = min(tpb, ext - t0);
-  const int row = wave * 32 + (lane & 31);
-  const int t = row / G, g = row % G;
-  const bool valid = row < tpb * G && t < ntok;
-  const int64_t qrow_idx = int64_t(qo + t0 + t) * Hq + kvh * G + g;
-  bf16x8 qf[D / 16];
-  load_q<D>(qf, q + qrow_idx * D, valid, lane);
-  WaveState<D> ws;
-  wave_init<D>(ws);
-  const int lim = valid ? prefix + t0 + t : -1;
-  const int key_end = prefix + t0 + ntok;
-  const int mask_from = prefix + t0 + 1;          // keys below this are visible to every row
-  const bool has_rows = wave * 32 < ntok * G;
-  const float c = sm_scale * kLog2e;
-  stream_keys<D, kExtKB, kExtNS, false>(ws, sm, qf, kpool + int64_t(kvh) * D, vpool + int64_t(kvh) * D, req_to_token + int64_t(b) * ld,
-                 Hkv, 0, key_end, mask_from, lim, c, has_rows, tid);
-  if (!valid) return;
-  float l = ws.l + __shfl_xor(ws.l, 32);
-  float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* orow = out + qrow_idx * D;
+  bf16x8 qf[2][D / 16];
+  int64_t qrow_idx[2];
+  bool valid[2];
+  ExtStream<D> a;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = wave * 64 + rb * 32 + (lane & 31);
+    const int t = row / G, g = row % G;
+    valid[rb] = row < tpb * G && t < ntok;
+    qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
+    load_q<D>(qf[rb], q + qrow_idx[rb] * D, valid[rb], lane);
+    a.lim[rb] = valid[rb] ? prefix + t0 + t : -1;
+  }
+  a.kc = reinterpret_cast<const char*>(kpool + int64_t(kvh) * D);
+  a.vc = reinterpret_cast<const char*>(vpool + int64_t(kvh) * D);
+  a.trow = req_to_token + int64_t(b) * ld;
+  a.row_bytes = uint32_t(Hkv) * D * 2;
+  a.lane = lane;
+  a.wave_u = __builtin_amdgcn_readfirstlane(wave);
+  a.jrow = lane / L::kChunks;
+  a.hik = 4 * (lane >> 5);
+#pragma unroll
+  for (int g = 0; g < L::kInstPerWave; ++g)
+    a.co[g] = 16u * uint32_t((lane % L::kChunks) ^ swz<D>(a.wave_u * L::kRowsPerWave + g * L::kRowsPerInst + a.jrow));
+  a.k1 = prefix + t0 + ntok;
+  a.ntiles = (a.k1 + kExtKB - 1) / kExtKB;
+  a.mask_from = prefix + t0 + 1;                  // keys below this are visible to every row
+  a.c = sm_scale * kLog2e;
+  const ExtOffsets<D> off = ext_offsets<D>(lane);
+  ExtState<D> es;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) es.o[rb][mb][j] = 0.f;
+    es.l[rb] = 0.f;
+    es.mx[rb] = -INFINITY;
+  }
+  es.guard = false;
+  // Q fragments and O accumulators live in AGPRs through the loop: only MFMAs read
+  // them there, which leaves the VGPRs to the scores, weights and addresses.
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[rb][ks]));
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
+  }
+  ext_pass<D>(es, sh, off, qf, a, true);
+  // The workgroup repeats the keys only if some weight of the first pass was too large,
+  // now with each row's true maximum as the reference.
+  if (__syncthreads_or(es.guard)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) es.o[rb][mb][j] = 0.f;
+      es.l[rb] = 0.f;
+      const float m = fmaxf(es.mx[rb], __shfl_xor(es.mx[rb], 32));
+      es.mc[rb] = (m == -INFINITY ? 0.f : m) * a.c;
+      es.lim[rb] = INFINITY;
+    }
+    ext_pass<D>(es, sh, off, qf, a, false);
+  }
   const int hi = lane >> 5;
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb)
+  for (int rb = 0; rb < 2; ++rb) {
+    if (!valid[rb]) continue;
+    const float l = es.l[rb] + __shfl_xor(es.l[rb], 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = out + qrow_idx[rb] * D;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      int d = mb * 32 + 8 * q4 + 4 * hi;
-      uint2 u;
-      u.x = pack_bf16(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv);
-      u.y = pack_bf16(ws.o[mb][4 * q4 + 2] * inv, ws.o[mb][4 * q4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d) = u;
-    }
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = mb * 32 + 8 * q4 + 4 * hi;
+        uint2 u;
+        u.x = pack_bf16(es.o[rb][mb][4 * q4 + 0] * inv, es.o[rb][mb][4 * q4 + 1] * inv);
+        u.y = pack_bf16(es.o[rb][mb][4 * q4 + 2] * inv, es.o[rb][mb][4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+  }
 }
 
 // ------------------------------------------------------------------ decode (bf16)
@@ -869,7 +1291,7 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     return rs::fail(RS_E_INVAL, "rs_extend_attention: null pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == RS_DTYPE_BF16) {
-    const int G = Hq / Hkv, tpb = 128 / G;
+    const int G = Hq / Hkv, tpb = kExtRows / G;
     const int n_qtiles = (max_extend_len + tpb - 1) / tpb;
     const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
     if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");

@@ -148,7 +148,8 @@ def _extend_case(torch, rs, Hq, Hkv, D, lens, dtname, seed):
     return worst
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 128), (8, 8, 128), (64, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 128), (8, 8, 128), (64, 8, 128), (8, 2, 64), (24, 8, 128),
+                                      (64, 4, 128), (128, 1, 64)])
 def test_extend_bf16_ragged(torch_rs, Hq, Hkv, D):
     torch, rs = torch_rs
     lens = [(0, 1), (0, 37), (1, 5), (63, 64), (64, 129), (200, 0), (517, 33), (1000, 300)]
@@ -164,6 +165,51 @@ def test_extend_f32_ragged(torch_rs, Hq, Hkv, D):
     _say(f"extend f32 Hq={Hq} Hkv={Hkv} D={D}")
     err = _extend_case(torch, rs, Hq, Hkv, D, lens, "f32", seed=7)
     assert err <= TOL["f32"], err
+
+
+def _planted_case(torch, rs, sm, lens, seed):
+    """Extend where one late key of each request is a scaled copy of its first query row,
+    so that row's late score stands far above every score of the first key tile."""
+    Hq, Hkv, D = 8, 2, 128
+    rng = np.random.default_rng(seed)
+    L = [p + e for p, e in lens]
+    S = sum(L) + 5
+    kp = _bf16(rng.standard_normal((S, Hkv, D)).astype(np.float32) * 0.1)
+    vp = _bf16(rng.standard_normal((S, Hkv, D)).astype(np.float32))
+    ext = np.array([e for _, e in lens], np.int32)
+    q = _bf16(rng.standard_normal((int(ext.sum()), Hq, D)).astype(np.float32))
+    qo = np.concatenate([[0], np.cumsum(ext)]).astype(np.int32)
+    perm = rng.permutation(S).astype(np.int32)
+    table = np.full((len(lens), max(L)), -1, np.int32)
+    off = 0
+    for b, n in enumerate(L):
+        table[b, :n] = perm[off:off + n]
+        off += n
+        p = lens[b][0]
+        kp[table[b, p - 7]] = q[qo[b], 0:Hq:Hq // Hkv]     # key p-7 of KV head h = query 0's head h*G
+    out = rs.extend_attention(_to_dev(torch, q, torch.bfloat16), _to_dev(torch, kp, torch.bfloat16),
+                              _to_dev(torch, vp, torch.bfloat16), _to_dev(torch, table, torch.int32),
+                              _to_dev(torch, qo, torch.int32),
+                              _to_dev(torch, np.array([p for p, _ in lens], np.int32), torch.int32),
+                              _to_dev(torch, ext, torch.int32), int(ext.max()), sm)
+    got = out.float().cpu().numpy()
+    worst = 0.0
+    for b, (p, e) in enumerate(lens):
+        row = table[b, :p + e]
+        o, _ = oracle.attend(q[qo[b]:qo[b + 1]], kp[row], vp[row], p + np.arange(e), sm)
+        worst = max(worst, float(np.abs(got[qo[b]:qo[b + 1]] - o).max()))
+    return worst
+
+
+@pytest.mark.parametrize("sm", [0.35, 1.0])
+def test_extend_late_dominant_key(torch_rs, sm):
+    """A late score ~45 (sm=0.35) or ~130 (sm=1) log2-units above the first tile's maximum:
+    exact either way, the larger one through the recomputation with the true row maximum."""
+    torch, rs = torch_rs
+    lens = [(100, 50), (700, 37), (3000, 64)]
+    _say(f"extend planted dominant key sm_scale={sm} lens={lens}")
+    err = _planted_case(torch, rs, sm, lens, seed=11)
+    assert err <= TOL["bf16"], err
 
 
 def test_extend_prefix_zero_is_textbook_causal(torch_rs):
