@@ -53,6 +53,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint16_t f2bf(float a) { return uint16_t(pack_bf16(a, 0.f) & 0xffffu); }
 
+// Max / sum of v over lanes l and l ^ 32.  v_permlane32_swap exchanges the upper half of
+// one operand with the lower half of the other; with v in both, the two results hold v of
+// lanes l and l ^ 32 (in some order), without a round trip through LDS.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One stage of a K/V tile in LDS: KB rows (keys) of K and of V, D*2 bytes each, unpadded.
 // Rows arrive straight from global memory with global_load_lds_dwordx4: one instruction
 // moves kRowsPerInst whole rows (lane l writes 16 bytes at M0 + 16*l), every lane with
@@ -437,11 +450,13 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 // diagonal or a ragged end, is masked.
 //
 // Softmax reference.  Each row's reference point is the maximum of its scores in tile 0
-// and stays fixed for the pass, so the loop never rescales O.  Later scores may exceed it:
-// weights up to 2^kExtGuard are exact in fp32 and bf16.  A lane that sees a larger excess
-// raises a guard flag, and if any lane of the workgroup did, a second pass recomputes the
-// rows with each row's true maximum as the reference (every weight <= 1).  Softmax does
-// not depend on the reference point.
+// and stays fixed for the pass, so the loop never rescales O and tracks no maximum.
+// Later scores may exceed it: the weights then exceed 1, which fp32 and bf16 carry with
+// the same relative precision up to their common overflow near 2^128.  Only an overflow
+// can spoil the result, and it leaves an inf or a NaN in O or l; the output check catches
+// that.  Then the workgroup finds each row's true maximum in a pass that tracks it and
+// recomputes its rows with that maximum as the reference (every weight <= 1).  Softmax
+// does not depend on the reference point.
 constexpr int kExtKB = 32;           // keys per tile
 constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
 constexpr int kExtRows = 256;        // query rows per workgroup: 4 waves x 64
@@ -450,16 +465,13 @@ constexpr int kExtAhead = kExtNS - 2;            // tiles in flight ahead of the
 constexpr int kExtSlotLead = 2 * kExtAhead + 1;  // slot ids are loaded this many tiles ahead
 constexpr int kExtRing = 16;                     // slot-id ring entries (tiles)
 static_assert(kExtRing >= kExtSlotLead && kExtRing > kExtAhead, "slot ring too small");
-constexpr float kExtGuard = 64.f;    // first-pass weights stay below 2^kExtGuard
 
 template <int D>
 struct ExtState {
   f32x16 o[2][D / 32];          // O^T per row block (layout as WaveState)
   float mc[2];                  // reference point times c, per row block (fixed per pass)
-  float lim[2];                 // guard: raw scores above this would weigh over 2^kExtGuard
-  float mx[2];                  // this lane's running maximum of raw scores
+  float mx[2];                  // this lane's running maximum of raw scores (tracking pass)
   float l[2];                   // this lane's halves of the running sums
-  bool guard;
 };
 
 struct Weights2 {
@@ -532,16 +544,14 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return m;
 }
 
-// Weights P = bf16(exp2(S*c - m*c)) of both row blocks, their row sums (of the bf16
-// weights, as the second MFMA sees them), the running maxima and the guard.
-template <int D>
+// Weights P = bf16(exp2(S*c - m*c)) of both row blocks and their row sums (of the bf16
+// weights, as the second MFMA sees them); TRACK: also the running maxima of the scores.
+template <int D, bool TRACK>
 __device__ __forceinline__ void ext_weights(Weights2& w, ExtState<D>& es, const f32x16 (&sc)[2], float c) {
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float tmax = max16(sc[rb]);
-    es.mx[rb] = fmaxf(es.mx[rb], tmax);
-    es.guard |= tmax > es.lim[rb];
+    if (TRACK) es.mx[rb] = fmaxf(es.mx[rb], max16(sc[rb]));
     float sum = 0.f;
 #pragma unroll
     for (int kstep = 0; kstep < kExtKB / 16; ++kstep) {
@@ -718,7 +728,7 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
 
 // Iterations [t_begin, t_end), t_begin >= 1: sprev holds S(t-1) in VGPRs on entry and
 // S(t_end-1) on exit.
-template <int D, bool MASK>
+template <int D, bool MASK, bool TRACK>
 __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
                                           const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[2],
                                           int t_begin, int t_end) {
@@ -732,7 +742,7 @@ __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, con
     f32x16 scur[2];
     ext_qk<D>(scur, kf, qf);
     Weights2 w;
-    ext_weights<D>(w, es, sprev, a.c);
+    ext_weights<D, TRACK>(w, es, sprev, a.c);
     ext_pv<D>(es, vf, w);
     ext_take_scores<D, MASK>(sprev, scur, a, t);
     __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
@@ -741,7 +751,9 @@ __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, con
 
 // One pass over keys [0, k1).  first_pass: the references come from tile 0's row maxima;
 // otherwise es.mc is already set.
-template <int D>
+// One pass over the keys.  first_pass: each row's reference point is its maximum over
+// tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
+template <int D, bool TRACK>
 __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
                                          const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, bool first_pass) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
@@ -768,21 +780,68 @@ __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, cons
     for (int rb = 0; rb < 2; ++rb) {
       float m = max16(sprev[rb]);
       m = fmaxf(m, __shfl_xor(m, 32));
-      const float m_ref = (m == -INFINITY) ? 0.f : m;
-      es.mc[rb] = m_ref * a.c;
-      es.lim[rb] = m_ref + kExtGuard / a.c;
+      es.mc[rb] = (m == -INFINITY ? 0.f : m) * a.c;
     }
   }
   const int t_split = max(1, t_mask);
-  ext_iters<D, false>(es, sh, off, qf, a, sprev, 1, t_split);
-  ext_iters<D, true>(es, sh, off, qf, a, sprev, t_split, a.ntiles);
+  ext_iters<D, false, TRACK>(es, sh, off, qf, a, sprev, 1, t_split);
+  ext_iters<D, true, TRACK>(es, sh, off, qf, a, sprev, t_split, a.ntiles);
   // the last tile's weights and P.V
   Weights2 w;
-  ext_weights<D>(w, es, sprev, a.c);
+  ext_weights<D, TRACK>(w, es, sprev, a.c);
   ext_pv<D>(es, ext_read_v<D>(sh.st[(a.ntiles - 1) % kExtNS].v, off), w);
   // the loads past the last tile have landed, and every wave is done with the stages and
   // the ring, before a later pass refills them or the workgroup ends
   wait_vmcnt_barrier<0>();
+}
+
+// Zero O and l; no maximum seen yet.
+template <int D>
+__device__ __forceinline__ void ext_reset(ExtState<D>& es) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) es.o[rb][mb][j] = 0.f;
+    es.l[rb] = 0.f;
+    es.mx[rb] = -INFINITY;
+  }
+}
+
+// Write the valid rows' outputs O / l (bf16).  Returns true if any of them, or l, is not
+// finite: only an overflow of the weights makes that happen (x * 0 is 0 for finite x and
+// NaN for inf or NaN, so z is NaN exactly then).
+template <int D>
+__device__ __forceinline__ bool ext_store(const ExtState<D>& es, const bool (&valid)[2], const int64_t (&qrow_idx)[2],
+                                          uint16_t* __restrict__ out, int lane) {
+  const int hi = lane >> 5;
+  float z = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    if (!valid[rb]) continue;
+    const float l = xhalf_sum(es.l[rb]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    z = fmaf(l, 0.f, z);
+    uint16_t* orow = out + qrow_idx[rb] * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = mb * 32 + 8 * q4 + 4 * hi;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = es.o[rb][mb][4 * q4 + e] * inv;
+          z = fmaf(v[e], 0.f, z);
+        }
+        uint2 u;
+        u.x = pack_bf16(v[0], v[1]);
+        u.y = pack_bf16(v[2], v[3]);
+        *reinterpret_cast<uint2*>(orow + d) = u;
+      }
+  }
+  return z != 0.f;                 // true for NaN
 }
 
 template <int D>
@@ -838,16 +897,7 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
   a.c = sm_scale * kLog2e;
   const ExtOffsets<D> off = ext_offsets<D>(lane);
   ExtState<D> es;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) es.o[rb][mb][j] = 0.f;
-    es.l[rb] = 0.f;
-    es.mx[rb] = -INFINITY;
-  }
-  es.guard = false;
+  ext_reset<D>(es);
   // Q fragments and O accumulators live in AGPRs through the loop: only MFMAs read
   // them there, which leaves the VGPRs to the scores, weights and addresses.
 #pragma unroll
@@ -857,40 +907,18 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
-  ext_pass<D>(es, sh, off, qf, a, true);
-  // The workgroup repeats the keys only if some weight of the first pass was too large,
-  // now with each row's true maximum as the reference.
-  if (__syncthreads_or(es.guard)) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) es.o[rb][mb][j] = 0.f;
-      es.l[rb] = 0.f;
-      const float m = fmaxf(es.mx[rb], __shfl_xor(es.mx[rb], 32));
-      es.mc[rb] = (m == -INFINITY ? 0.f : m) * a.c;
-      es.lim[rb] = INFINITY;
-    }
-    ext_pass<D>(es, sh, off, qf, a, false);
-  }
-  const int hi = lane >> 5;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    if (!valid[rb]) continue;
-    const float l = es.l[rb] + __shfl_xor(es.l[rb], 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = out + qrow_idx[rb] * D;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = mb * 32 + 8 * q4 + 4 * hi;
-        uint2 u;
-        u.x = pack_bf16(es.o[rb][mb][4 * q4 + 0] * inv, es.o[rb][mb][4 * q4 + 1] * inv);
-        u.y = pack_bf16(es.o[rb][mb][4 * q4 + 2] * inv, es.o[rb][mb][4 * q4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = u;
-      }
+  for (int pass = 0;; ++pass) {
+    ext_pass<D, false>(es, sh, off, qf, a, pass == 0);
+    const bool overflow = ext_store<D>(es, valid, qrow_idx, out, lane);
+    if (pass == 1 || !__syncthreads_or(overflow)) break;
+    // Some weight overflowed: find each row's true maximum, then recompute the rows
+    // with it as the reference (the outputs above are overwritten).
+    ext_reset<D>(es);
+    ext_pass<D, true>(es, sh, off, qf, a, true);
+    const float mx0 = xhalf_max(es.mx[0]), mx1 = xhalf_max(es.mx[1]);
+    ext_reset<D>(es);
+    es.mc[0] = (mx0 == -INFINITY ? 0.f : mx0) * a.c;
+    es.mc[1] = (mx1 == -INFINITY ? 0.f : mx1) * a.c;
   }
 }
 

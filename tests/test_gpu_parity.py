@@ -201,10 +201,11 @@ def _planted_case(torch, rs, sm, lens, seed):
     return worst
 
 
-@pytest.mark.parametrize("sm", [0.35, 1.0])
+@pytest.mark.parametrize("sm", [0.35, 0.6, 1.0])
 def test_extend_late_dominant_key(torch_rs, sm):
-    """A late score ~45 (sm=0.35) or ~130 (sm=1) log2-units above the first tile's maximum:
-    exact either way, the larger one through the recomputation with the true row maximum."""
+    """A late score far above the first tile's maximum (about 0.35, 0.6 or 1.0 x 185
+    log2-units): weights up to ~2^110 stay finite and exact relative to each other; at
+    sm=1 they overflow fp32, and the rows are recomputed with their true maximum."""
     torch, rs = torch_rs
     lens = [(100, 50), (700, 37), (3000, 64)]
     _say(f"extend planted dominant key sm_scale={sm} lens={lens}")
