@@ -704,6 +704,16 @@ __device__ __forceinline__ void ext_wait(int t) {
   else wait_vmcnt_barrier<0>();
 }
 
+// Iteration t of the loop waits for tile t + 1 (its K is read ahead, at the end of
+// iteration t).  Tile t + 1 was issued by iteration t + 1 - kExtAhead (iteration 0 being
+// the tile-0 step), and kExtAhead - 2 iterations' loads came after it.
+template <int D>
+__device__ __forceinline__ void ext_wait_next(int t) {
+  constexpr int kAfter = (kExtAhead - 2) * (1 + 2 * StageLayout<D, kExtKB>::kInstPerWave);
+  if (t + 1 >= kExtAhead) wait_vmcnt_barrier<kAfter>();
+  else wait_vmcnt_barrier<0>();
+}
+
 // Scores of tile t to VGPRs (the next iteration's operand) and, for MASK, -inf past this
 // lane's last visible key or the tile's last key.
 template <int D, bool MASK>
@@ -728,15 +738,16 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
 
 // Iterations [t_begin, t_end), t_begin >= 1: sprev holds S(t-1) in VGPRs on entry and
 // S(t_end-1) on exit.
+// Iterations [t_begin, t_end).  On entry kf holds K(t_begin) and vf V(t_begin - 1); each
+// iteration reads the next ones at its end, after its MFMAs are issued, so their LDS
+// latency overlaps the matrix work instead of delaying the next iteration's first MFMA.
 template <int D, bool MASK, bool TRACK>
 __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
                                           const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[2],
-                                          int t_begin, int t_end) {
+                                          KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
   for (int t = t_begin; t < t_end; ++t) {
-    ext_wait<D>(t);
+    ext_wait_next<D>(t);
     const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, t + kExtAhead);
-    const KFrags<D> kf = ext_read_k<D>(sh.st[t % kExtNS].k, off);
-    const VFrags<D> vf = ext_read_v<D>(sh.st[(t - 1) % kExtNS].v, off);
     ext_slot_dma<D>(sh, a, t + kExtSlotLead);
     ext_kv_dma<D>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
     f32x16 scur[2];
@@ -744,6 +755,8 @@ __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, con
     Weights2 w;
     ext_weights<D, TRACK>(w, es, sprev, a.c);
     ext_pv<D>(es, vf, w);
+    kf = ext_read_k<D>(sh.st[(t + 1) % kExtNS].k, off);
+    vf = ext_read_v<D>(sh.st[t % kExtNS].v, off);
     ext_take_scores<D, MASK>(sprev, scur, a, t);
     __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
   }
@@ -766,12 +779,18 @@ __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, cons
   ext_wait<D>(0);
   ext_slot_dma<D>(sh, a, kExtSlotLead);
   f32x16 sprev[2];
+  KFrags<D> kf;
+  VFrags<D> vf;
   {
     const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, kExtAhead);
-    const KFrags<D> kf = ext_read_k<D>(sh.st[0].k, off);
+    kf = ext_read_k<D>(sh.st[0].k, off);
     ext_kv_dma<D>(sh.st[kExtAhead % kExtNS], a, sl);
     f32x16 scur[2];
     ext_qk<D>(scur, kf, qf);
+    // every prologue tile has landed (the wait above counted to zero): tile 1's K and
+    // tile 0's V for the first iteration
+    kf = ext_read_k<D>(sh.st[1 % kExtNS].k, off);
+    vf = ext_read_v<D>(sh.st[0].v, off);
     if (t_mask == 0) ext_take_scores<D, true>(sprev, scur, a, 0);
     else ext_take_scores<D, false>(sprev, scur, a, 0);
   }
@@ -784,12 +803,12 @@ __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, cons
     }
   }
   const int t_split = max(1, t_mask);
-  ext_iters<D, false, TRACK>(es, sh, off, qf, a, sprev, 1, t_split);
-  ext_iters<D, true, TRACK>(es, sh, off, qf, a, sprev, t_split, a.ntiles);
-  // the last tile's weights and P.V
+  ext_iters<D, false, TRACK>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
+  ext_iters<D, true, TRACK>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
+  // the last tile's weights and P.V (vf holds its V)
   Weights2 w;
   ext_weights<D, TRACK>(w, es, sprev, a.c);
-  ext_pv<D>(es, ext_read_v<D>(sh.st[(a.ntiles - 1) % kExtNS].v, off), w);
+  ext_pv<D>(es, vf, w);
   // the loads past the last tile have landed, and every wave is done with the stages and
   // the ring, before a later pass refills them or the workgroup ends
   wait_vmcnt_barrier<0>();
