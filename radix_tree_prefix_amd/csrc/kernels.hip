@@ -627,7 +627,7 @@ struct ExtStream {
 template <int D>
 struct ExtShared {
   Stage<D, kExtKB> st[kExtNS];
-  int32_t ring[kExtRing][kExtWaves][64];   // per tile and wave: its 8 slot ids, repeated
+  int32_t ring[kExtRing][kExtWaves][kExtKB / kExtWaves];   // per tile and wave: its slot ids
 };
 
 // Global -> LDS loads issued through inline assembly.  The LDS address goes through M0,
@@ -653,13 +653,16 @@ __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {    // l
 }
 #pragma clang diagnostic pop
 
-// Slot ids of tile x into this wave's ring row: lane l loads the id of key 8*wave + l%8
-// (a full-wave load, no branch); keys past k1 repeat the last slot.
+// Slot ids of tile x into this wave's ring row: lane l < 8 loads the id of key 8*wave + l;
+// keys past k1 repeat the last slot.
 template <int D>
 __device__ __forceinline__ void ext_slot_dma(ExtShared<D>& sh, const ExtStream<D>& a, int x) {
   constexpr int kPerWave = kExtKB / kExtWaves;
-  const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * kPerWave + (a.lane % kPerWave), a.k1 - 1);
-  dma_b32(src, lds_addr(&sh.ring[x % kExtRing][a.wave_u][0]));
+  // lanes 0 .. kPerWave-1 load (one instruction per wave all the same, so the waits count)
+  if (a.lane < kPerWave) {
+    const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * kPerWave + a.lane, a.k1 - 1);
+    dma_b32(src, lds_addr(&sh.ring[x % kExtRing][a.wave_u][0]));
+  }
 }
 
 // This lane's slot id for each of its DMA instructions of tile x, from the ring.
