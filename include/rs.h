@@ -159,6 +159,32 @@ int rs_stats(const rs_tree* t, rs_stats_t* out);
  * the NUL) to *need. */
 int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need);
 
+/* ------------------------------------------------------------------ scheduling */
+
+/* Order of a waiting queue [T "The scheduler is where the cache is won or lost"].
+ * Request i's tokens are tokens[offsets[i] .. offsets[i+1]) (host; offsets has n+1
+ * non-decreasing entries).  Each request's longest cached prefix is found without
+ * changing the tree (no split, no clock tick) and written to out_matched[i] (host,
+ * nullable).  out_order (host, n) receives a permutation of 0..n-1, first to run first:
+ *  RS_SCHED_FCFS        arrival order;
+ *  RS_SCHED_LPM         longest cached prefix first, ties in arrival order.  A request
+ *                       whose cached prefix is <= RS_SCHED_IN_QUEUE_THRESHOLD tokens and
+ *                       which shares that many leading tokens with an earlier such request
+ *                       (not itself put back) goes to the back, in arrival order, so that
+ *                       the earlier one fills the cache first.  Above
+ *                       RS_SCHED_LPM_MAX_QUEUE requests: arrival order;
+ *  RS_SCHED_DFS_WEIGHT  depth-first over the tree: a request hangs off the deepest node
+ *                       whose whole root path it matches; a node weighs the requests in
+ *                       its subtree; children of larger weight first (equal: ascending
+ *                       first token), a node's own requests after its subtrees, in
+ *                       arrival order.
+ * The tree is only read.  RS_E_INVAL for bad arguments or an unknown policy. */
+enum { RS_SCHED_FCFS = 0, RS_SCHED_LPM = 1, RS_SCHED_DFS_WEIGHT = 2 };
+#define RS_SCHED_LPM_MAX_QUEUE 128
+#define RS_SCHED_IN_QUEUE_THRESHOLD 32
+int rs_schedule(const rs_tree* t, const int32_t* tokens, const int64_t* offsets, int32_t n,
+                int32_t policy, int32_t* out_order, int64_t* out_matched);
+
 /* ------------------------------------------------------------------ decode plan */
 
 /* Segments of a decode batch from the tree [L "How the runtime and frontend work

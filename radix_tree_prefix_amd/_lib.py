@@ -21,6 +21,7 @@ if not os.path.exists(LIB_PATH):
 lib = C.CDLL(LIB_PATH)
 
 RS_OK, RS_E_INVAL, RS_E_NOSPACE, RS_E_STALE, RS_E_HIP, RS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+SCHED_POLICIES = {"fcfs": 0, "lpm": 1, "dfs-weight": 2}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 _NAMES = {RS_E_INVAL: "RS_E_INVAL", RS_E_NOSPACE: "RS_E_NOSPACE", RS_E_STALE: "RS_E_STALE",
           RS_E_HIP: "RS_E_HIP", RS_E_UNSUPPORTED: "RS_E_UNSUPPORTED"}
@@ -84,6 +85,7 @@ _SIGS = {
     "rs_admit": (C.c_int, [_P, _P, C.c_int64, C.c_int64, _P, _I64P, _I64P]),
     "rs_stats": (C.c_int, [_P, C.POINTER(Stats)]),
     "rs_tree_dump": (C.c_int, [_P, C.c_char_p, C.c_int64, _I64P]),
+    "rs_schedule": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, _P, _P]),
     "rs_decode_plan_build": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                        C.POINTER(C.c_void_p)]),
     "rs_plan_info": (C.c_int, [_P, C.POINTER(PlanInfo)]),
@@ -185,6 +187,20 @@ class Tree:
         _check(lib.rs_admit(self._h, tp, int(cached), int(new), row.ctypes.data_as(C.c_void_p),
                             C.byref(node), C.byref(m)))
         return row, node.value, m.value
+
+    def schedule(self, queue, policy="lpm"):
+        """Order of a waiting queue (list of token arrays): (order, matched) from rs_schedule."""
+        lens = np.array([len(q) for q in queue], np.int64)
+        offs = np.zeros(len(queue) + 1, np.int64)
+        np.cumsum(lens, out=offs[1:])
+        tok = np.ascontiguousarray(np.concatenate([np.asarray(q, np.int32) for q in queue]) if len(queue)
+                                   else np.zeros(0, np.int32), dtype=np.int32)
+        order = np.empty(len(queue), np.int32)
+        matched = np.empty(len(queue), np.int64)
+        _check(lib.rs_schedule(self._h, tok.ctypes.data_as(C.c_void_p), offs.ctypes.data_as(C.c_void_p),
+                               len(queue), SCHED_POLICIES[policy], order.ctypes.data_as(C.c_void_p),
+                               matched.ctypes.data_as(C.c_void_p)))
+        return order, matched
 
     def stats(self):
         s = Stats()

@@ -16,6 +16,9 @@ void set_error(const std::string& msg);
 void clear_error();
 int fail(int code, const std::string& msg);
 
+// Index of the first position where a[0..n) and b[0..n) differ (n if none).
+int64_t diverge(const int32_t* a, const int32_t* b, int64_t n);
+
 // ---------------------------------------------------------------- radix tree
 
 struct Node {

@@ -41,7 +41,7 @@ int fail(int code, const std::string& msg) {
 // Index of the first position where a and b differ (n if none).  Galloping:
 // windows [0,1), [1,3), [3,7), ... are compared whole; the first window that
 // differs is bisected with whole-span compares.
-static int64_t diverge(const int32_t* a, const int32_t* b, int64_t n) {
+int64_t diverge(const int32_t* a, const int32_t* b, int64_t n) {
   int64_t lo = 0, w = 1;
   while (lo < n) {
     int64_t len = std::min(w, n - lo);
