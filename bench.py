@@ -68,6 +68,19 @@ def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
         tree.dec_lock_ref(node)
     st.history_s = time.perf_counter() - t0
 
+    # cache-aware ordering of the batch as a waiting queue (its cached parts) on this tree
+    from radix_tree_prefix_amd._lib import pack_queue
+    queue = [r.tokens[:r.cached] for r in wl.requests]
+    packed = pack_queue(queue[:128])
+    t0 = time.perf_counter()
+    tree.schedule_packed(*packed, "lpm")
+    st.sched_lpm_s = time.perf_counter() - t0
+    packed = pack_queue(queue)
+    t0 = time.perf_counter()
+    tree.schedule_packed(*packed, "dfs-weight")
+    st.sched_dfs_s = time.perf_counter() - t0
+    st.sched_n = len(queue)
+
     # batch: admit every request in order, its slots straight into its table row
     # table rows padded to 64 bytes, as an engine allocates its request-to-token pool
     ld = -(-max(r.seq_len for r in wl.requests) // 16) * 16
@@ -380,7 +393,9 @@ def main():
         "roofline": roof,
         "parts_ms": {"store_kv": round(store_ms, 4), "extend": round(ext_ms, 4), "decode": round(dec_ms, 4)},
         "host_ms": {"history_admission": round(st.history_s * 1e3, 2), "batch_admission": round(st.admit_s * 1e3, 3),
-                    "decode_plan": round(getattr(st, "plan_s", 0.0) * 1e3, 3)},
+                    "decode_plan": round(getattr(st, "plan_s", 0.0) * 1e3, 3),
+                    f"schedule_lpm_{min(st.sched_n, 128)}": round(st.sched_lpm_s * 1e3, 3),
+                    f"schedule_dfs_weight_{st.sched_n}": round(st.sched_dfs_s * 1e3, 3)},
     }
     if st.dec:
         out["decode_hbm"] = {"achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

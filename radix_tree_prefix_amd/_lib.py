@@ -121,6 +121,14 @@ def _i64(a):
     return a, a.ctypes.data_as(C.c_void_p)
 
 
+def pack_queue(queue):
+    """A list of token sequences as (int32 tokens, int64 offsets[n+1]) for rs_schedule."""
+    offs = np.zeros(len(queue) + 1, np.int64)
+    np.cumsum([len(q) for q in queue], out=offs[1:])
+    tok = np.concatenate([np.asarray(q, np.int32) for q in queue]) if len(queue) else np.zeros(0, np.int32)
+    return tok, offs
+
+
 # ------------------------------------------------------------------ tree
 class Tree:
     """Host radix tree over pool slots 0..pool_slots-1 (rs_tree_* calls)."""
@@ -190,15 +198,16 @@ class Tree:
 
     def schedule(self, queue, policy="lpm"):
         """Order of a waiting queue (list of token arrays): (order, matched) from rs_schedule."""
-        lens = np.array([len(q) for q in queue], np.int64)
-        offs = np.zeros(len(queue) + 1, np.int64)
-        np.cumsum(lens, out=offs[1:])
-        tok = np.ascontiguousarray(np.concatenate([np.asarray(q, np.int32) for q in queue]) if len(queue)
-                                   else np.zeros(0, np.int32), dtype=np.int32)
-        order = np.empty(len(queue), np.int32)
-        matched = np.empty(len(queue), np.int64)
-        _check(lib.rs_schedule(self._h, tok.ctypes.data_as(C.c_void_p), offs.ctypes.data_as(C.c_void_p),
-                               len(queue), SCHED_POLICIES[policy], order.ctypes.data_as(C.c_void_p),
+        return self.schedule_packed(*pack_queue(queue), policy)
+
+    def schedule_packed(self, tokens, offsets, policy="lpm"):
+        """rs_schedule on a queue already packed as (int32 tokens, int64 offsets[n+1])."""
+        tok, tp = _i32(tokens)
+        offs, op = _i64(offsets)
+        n = len(offs) - 1
+        order = np.empty(n, np.int32)
+        matched = np.empty(n, np.int64)
+        _check(lib.rs_schedule(self._h, tp, op, n, SCHED_POLICIES[policy], order.ctypes.data_as(C.c_void_p),
                                matched.ctypes.data_as(C.c_void_p)))
         return order, matched
 
