@@ -255,6 +255,41 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool,
  * extend_lens: host int32 [B]; order: host int32 [B] out. */
 int rs_extend_order(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B, int32_t* order);
 
+/* ------------------------------------------------------------------ draft-tree verify */
+
+/* Host: the draft tree of a verify step [T "Speculative decoding puts a tree inside the
+ * tree"].  Each of the B requests verifies n <= 64 tokens; parents (host int32 [B][n])
+ * gives token i's parent, with token 0 the root (parent -1: the last verified token) and
+ * every other parent in 0..i-1.  Outputs (host, [B][n]): tree_mask, bit j set iff token j
+ * is token i or one of its ancestors; positions = prefix_lens[b] + depth (root depth 0;
+ * depths [0,1,1,2] after a 7-token prompt give [7,8,8,9]); next_token = first child,
+ * next_sibling = the next child of the same parent in index order (-1: none).
+ * RS_E_INVAL if a parent is out of range. */
+int rs_draft_tree_build(const int32_t* parents, const int32_t* prefix_lens, int32_t B, int32_t n,
+                        uint64_t* tree_mask, int32_t* positions, int32_t* next_token,
+                        int32_t* next_sibling);
+
+/* Verify attention: request b's n tokens (q rows b*n .. b*n+n-1, device [B*n][Hq][D])
+ * attend to cached positions 0..prefix_lens[b]-1 and, among the verify tokens (table
+ * positions prefix + j, their K/V stored first), to token i itself and its ancestors:
+ * token i sees verify token j iff bit j of tree_mask[b*n + i] is set and j <= i
+ * [T "Speculative decoding ..."]: one target pass checks every branch.  prefix_lens
+ * (device int32 [B]), tree_mask (device uint64 [B*n], from rs_draft_tree_build), out
+ * (device [B*n][Hq][D]).  bf16 only (RS_E_UNSUPPORTED otherwise); n <= 64. */
+int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* req_to_token, int64_t ld, const int32_t* prefix_lens,
+                             const uint64_t* tree_mask, int32_t B, int32_t n, int32_t Hq,
+                             int32_t Hkv, int32_t D, float sm_scale, int32_t dtype, void* out,
+                             void* stream);
+
+/* Copy pool rows src_slots[r] -> dst_slots[r] in both pools (device int32 [n] each): the
+ * accepted path of a draft tree is scattered over the draft's slots, and the radix tree
+ * adopts a token run only with its own run of slots, so the accepted KV is compacted
+ * first [T "Speculative decoding ..."].  Every dst slot must differ from every other dst
+ * slot and from every src slot at another index; otherwise the result is undefined. */
+int rs_move_kv(void* k_pool, void* v_pool, const int32_t* src_slots, const int32_t* dst_slots,
+               int64_t n, int32_t Hkv, int32_t D, int32_t dtype, void* stream);
+
 /* Decode attention: one query per request at position seq_lens[b]-1 over positions
  * 0..seq_lens[b]-1 (its own KV stored first) [L "A quick recap"].  q, out: device
  * [B][Hq][D]; lse_out: device float [B][Hq] natural-log log-sum-exp, or NULL.

@@ -11,3 +11,4 @@ from .attention import attend, merge_states  # noqa: F401
 from .admit import (admit, release, admit_history, admit_batch,  # noqa: F401
                     prefill_no_sharing, prefill_sequential, prefill_fixed_prefix)
 from .schedule import schedule, peek_match  # noqa: F401
+from . import speculative  # noqa: F401

@@ -11,10 +11,11 @@ import torch
 
 from . import _lib
 from ._lib import (Tree, Plan, RsError, NoSpaceError, StaleError, DTYPE_F32, DTYPE_BF16,  # noqa: F401
-                   decode_workspace_bytes, extend_order, LIB_PATH)
+                   decode_workspace_bytes, extend_order, draft_tree_build, LIB_PATH)
 
 __all__ = ["Tree", "Plan", "RsError", "NoSpaceError", "StaleError", "store_kv", "extend_attention",
-           "decode_attention", "merge_states", "DecodeWorkspace", "LIB_PATH"]
+           "decode_attention", "merge_states", "DecodeWorkspace", "draft_tree_build", "tree_verify_attention",
+           "move_kv", "LIB_PATH"]
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -60,6 +61,33 @@ def extend_attention(q, k_pool, v_pool, req_to_token, qo_indptr, prefix_lens, ex
                           _dtype(k_pool), _dev(out, "out", k_pool.dtype),
                           order=_dev(order, "order", torch.int32) if order is not None else None, stream=_stream(stream))
     return out
+
+
+def tree_verify_attention(q, k_pool, v_pool, req_to_token, prefix_lens, tree_mask, sm_scale, out=None,
+                          stream=None):
+    """q [B*n, Hq, D]; req_to_token int32 [B, ld] (row b: prefix slots, then the n verify tokens' slots);
+    prefix_lens int32 [B]; tree_mask uint64-as-int64 [B, n] (device, from draft_tree_build)."""
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    B, ld = req_to_token.shape
+    n = tree_mask.shape[1]
+    assert T == B * n and tree_mask.shape[0] == B
+    out = torch.empty_like(q) if out is None else out
+    _lib.tree_verify_attention(_dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                               _dev(v_pool, "v_pool", k_pool.dtype), _dev(req_to_token, "req_to_token", torch.int32),
+                               ld, _dev(prefix_lens, "prefix_lens", torch.int32), _dev(tree_mask, "tree_mask",
+                                                                                     torch.int64),
+                               B, n, Hq, Hkv, D, sm_scale, _dtype(k_pool), _dev(out, "out", k_pool.dtype),
+                               _stream(stream))
+    return out
+
+
+def move_kv(k_pool, v_pool, src_slots, dst_slots, stream=None):
+    """Copy pool rows src_slots[r] -> dst_slots[r] (device int32 [n]) in both pools."""
+    S, Hkv, D = k_pool.shape
+    _lib.move_kv(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+                 _dev(src_slots, "src_slots", torch.int32), _dev(dst_slots, "dst_slots", torch.int32),
+                 src_slots.numel(), Hkv, D, _dtype(k_pool), _stream(stream))
 
 
 class DecodeWorkspace:

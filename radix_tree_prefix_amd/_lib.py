@@ -99,6 +99,10 @@ _SIGS = {
     "rs_extend_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P, _P]),
     "rs_extend_order": (C.c_int, [_P, _P, C.c_int32, _P]),
+    "rs_draft_tree_build": (C.c_int, [_P, _P, C.c_int32, C.c_int32, _P, _P, _P, _P]),
+    "rs_tree_verify_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, _P, C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P]),
+    "rs_move_kv": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
     "rs_decode_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_float, C.c_int32, _P, _P, _P, C.c_int64, _P, _P, _P]),
     "rs_merge_states": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P]),
@@ -288,6 +292,32 @@ def extend_attention(q, k_pool, v_pool, req_to_token, ld, qo_indptr, prefix_lens
     _check(lib.rs_extend_attention(q, k_pool, v_pool, req_to_token, int(ld), qo_indptr, prefix_lens, extend_lens,
                                    int(B), int(max_extend_len), int(Hq), int(Hkv), int(D), float(sm_scale),
                                    int(dtype), order, out, C.c_void_p(stream)))
+
+
+def draft_tree_build(parents, prefix_lens):
+    """Host: (tree_mask uint64, positions, next_token, next_sibling), each [B, n], of draft trees
+    given by parents (int32 [B, n], token 0 the root with parent -1)."""
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    B, n = par.shape
+    pl, plp = _i32(prefix_lens)
+    assert len(pl) == B
+    mask = np.empty((B, n), np.uint64)
+    pos, nt, ns = (np.empty((B, n), np.int32) for _ in range(3))
+    _check(lib.rs_draft_tree_build(par.ctypes.data_as(C.c_void_p), plp, B, n, mask.ctypes.data_as(C.c_void_p),
+                                   pos.ctypes.data_as(C.c_void_p), nt.ctypes.data_as(C.c_void_p),
+                                   ns.ctypes.data_as(C.c_void_p)))
+    return mask, pos, nt, ns
+
+
+def tree_verify_attention(q, k_pool, v_pool, req_to_token, ld, prefix_lens, tree_mask, B, n, Hq, Hkv, D, sm_scale,
+                          dtype, out, stream=0):
+    _check(lib.rs_tree_verify_attention(q, k_pool, v_pool, req_to_token, int(ld), prefix_lens, tree_mask, int(B),
+                                        int(n), int(Hq), int(Hkv), int(D), float(sm_scale), int(dtype), out,
+                                        C.c_void_p(stream)))
+
+
+def move_kv(k_pool, v_pool, src, dst, n, Hkv, D, dtype, stream=0):
+    _check(lib.rs_move_kv(k_pool, v_pool, src, dst, int(n), int(Hkv), int(D), int(dtype), C.c_void_p(stream)))
 
 
 def extend_order(prefix_lens, extend_lens):

@@ -621,6 +621,11 @@ struct ExtStream {
   int hik;                    // 4 in the upper lane half: its score elements sit 4 keys later
   int lim[2];                 // last visible key position of this lane's row per block (-1: none)
   float c;
+  // draft-tree verify: keys at and past tree_base are visible to a row only where its
+  // ancestor mask has their bit (key - tree_base); tree = false: plain causal
+  bool tree;
+  int tree_base;
+  uint64_t tm[2];
 };
 
 // LDS of the extend workgroup: the K/V stages and the slot-id ring.
@@ -732,9 +737,21 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int thr = min(a.lim[rb] - key0, nk - 1) - a.hik;
+      if (a.tree) {
+        // key k = key0 + hik + ext_key(j): causal bound as above, and past tree_base only
+        // the keys of the row's ancestor mask
+        const int rel0 = key0 + a.hik - a.tree_base;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (ext_key(j) > thr) dst[rb][j] = -INFINITY;
+        for (int j = 0; j < 16; ++j) {
+          const int rel = rel0 + ext_key(j);
+          const bool in_tree = rel < 0 || (rel < 64 && ((a.tm[rb] >> (rel & 63)) & 1));
+          if (ext_key(j) > thr || !in_tree) dst[rb][j] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (ext_key(j) > thr) dst[rb][j] = -INFINITY;
+      }
     }
   }
 }
@@ -866,12 +883,14 @@ __device__ __forceinline__ bool ext_store(const ExtState<D>& es, const bool (&va
   return z != 0.f;                 // true for NaN
 }
 
-template <int D>
+// TREE: draft-tree verify (tree_mask gives each row's ancestor mask); otherwise causal.
+template <int D, bool TREE>
 __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
-    int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out) {
+    int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out, int uniform_n,
+    const uint64_t* __restrict__ tree_mask) {
   static_assert(kThreads == 64 * kExtWaves, "one wave per 64 rows");
   __shared__ ExtShared<D> sh;
   using L = StageLayout<D, kExtKB>;
@@ -883,16 +902,19 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
   // requests in the given order; within a request the later (longer) q-tiles first
   const int qt = n_qtiles - 1 - rest % n_qtiles, i = rest / n_qtiles;
   const int b = order ? order[i] : i;
-  const int ext = extend_lens[b];
+  // uniform_n > 0: every request computes uniform_n tokens, packed in request order
+  const int ext = uniform_n > 0 ? uniform_n : extend_lens[b];
   const int t0 = qt * tpb;
   if (t0 >= ext) return;
   const int prefix = prefix_lens[b];
-  const int qo = qo_indptr[b];
+  const int qo = uniform_n > 0 ? b * uniform_n : qo_indptr[b];
   const int ntok = min(tpb, ext - t0);
+  ExtStream<D> a;
+  a.tree = TREE;
+  a.tree_base = prefix;
   bf16x8 qf[2][D / 16];
   int64_t qrow_idx[2];
   bool valid[2];
-  ExtStream<D> a;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int row = wave * 64 + rb * 32 + (lane & 31);
@@ -901,6 +923,7 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
     load_q<D>(qf[rb], q + qrow_idx[rb] * D, valid[rb], lane);
     a.lim[rb] = valid[rb] ? prefix + t0 + t : -1;
+    a.tm[rb] = (a.tree && valid[rb]) ? tree_mask[qo + t0 + t] : 0ull;
   }
   a.kc = reinterpret_cast<const char*>(kpool + int64_t(kvh) * D);
   a.vc = reinterpret_cast<const char*>(vpool + int64_t(kvh) * D);
@@ -915,7 +938,7 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     a.co[g] = 16u * uint32_t((lane % L::kChunks) ^ swz<D>(a.wave_u * L::kRowsPerWave + g * L::kRowsPerInst + a.jrow));
   a.k1 = prefix + t0 + ntok;
   a.ntiles = (a.k1 + kExtKB - 1) / kExtKB;
-  a.mask_from = prefix + t0 + 1;                  // keys below this are visible to every row
+  a.mask_from = a.tree ? prefix : prefix + t0 + 1;   // keys below this are visible to every row
   a.c = sm_scale * kLog2e;
   const ExtOffsets<D> off = ext_offsets<D>(lane);
   ExtState<D> es;
@@ -1263,6 +1286,19 @@ __global__ void store_kv_kernel(uint4* __restrict__ kpool, uint4* __restrict__ v
   }
 }
 
+// Pool rows src[r] -> dst[r], both pools, 16 bytes per thread step.
+__global__ void move_kv_kernel(uint4* __restrict__ kpool, uint4* __restrict__ vpool, const int32_t* __restrict__ src,
+                               const int32_t* __restrict__ dst, int64_t n, int row_chunks) {
+  const int64_t total = n * row_chunks;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = e / row_chunks, c = e % row_chunks;
+    const int64_t from = int64_t(src[r]) * row_chunks + c, to = int64_t(dst[r]) * row_chunks + c;
+    const uint4 k = kpool[from], v = vpool[from];
+    kpool[to] = k;
+    vpool[to] = v;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ float ld_as_f32(const T* p, int64_t i);
 template <>
@@ -1330,6 +1366,48 @@ int rs_store_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new
   return hip_check("rs_store_kv");
 }
 
+int rs_move_kv(void* k_pool, void* v_pool, const int32_t* src_slots, const int32_t* dst_slots, int64_t n, int32_t Hkv,
+               int32_t D, int32_t dtype, void* stream) {
+  if (n < 0 || Hkv <= 0 || D <= 0) return rs::fail(RS_E_INVAL, "rs_move_kv: bad sizes");
+  if (dtype != RS_DTYPE_F32 && dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_move_kv: dtype");
+  const int64_t row_bytes = int64_t(Hkv) * D * (dtype == RS_DTYPE_F32 ? 4 : 2);
+  if (row_bytes % 16) return rs::fail(RS_E_UNSUPPORTED, "rs_move_kv: a pool row must be a multiple of 16 bytes");
+  if (n == 0) return RS_OK;
+  if (!k_pool || !v_pool || !src_slots || !dst_slots) return rs::fail(RS_E_INVAL, "rs_move_kv: null pointer");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return rs::fail(RS_E_INVAL, "rs_move_kv: pools must be 16-byte aligned");
+  const int rc = int(row_bytes / 16);
+  hipLaunchKernelGGL(move_kv_kernel, dim3(grid_for(n * rc, 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), src_slots, dst_slots, n, rc);
+  return hip_check("rs_move_kv");
+}
+
+int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                             int64_t ld, const int32_t* prefix_lens, const uint64_t* tree_mask, int32_t B, int32_t n,
+                             int32_t Hq, int32_t Hkv, int32_t D, float sm_scale, int32_t dtype, void* out,
+                             void* stream) {
+  if (B < 0 || n < 0 || n > 64 || ld <= 0) return rs::fail(RS_E_INVAL, "rs_tree_verify_attention: bad sizes");
+  if (!dims_ok(Hq, Hkv, D)) return rs::fail(RS_E_UNSUPPORTED, "rs_tree_verify_attention: heads/head_dim unsupported");
+  if (dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_tree_verify_attention: bf16 only");
+  if (B == 0 || n == 0) return RS_OK;
+  if (!q || !k_pool || !v_pool || !req_to_token || !prefix_lens || !tree_mask || !out)
+    return rs::fail(RS_E_INVAL, "rs_tree_verify_attention: null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = Hq / Hkv, tpb = kExtRows / G;
+  const int n_qtiles = (n + tpb - 1) / tpb;
+  const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
+  if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_tree_verify_attention: grid too large");
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), req_to_token, ld,
+                       nullptr, prefix_lens, nullptr, n_qtiles, Hq, Hkv, sm_scale, nullptr,
+                       static_cast<uint16_t*>(out), int(n), tree_mask);
+  };
+  if (D == 128) args(extend_bf16_kernel<128, true>);
+  else args(extend_bf16_kernel<64, true>);
+  return hip_check("rs_tree_verify_attention");
+}
+
 int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
                         int64_t ld, const int32_t* qo_indptr, const int32_t* prefix_lens, const int32_t* extend_lens,
                         int32_t B, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
@@ -1349,10 +1427,10 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
       hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
                          static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), req_to_token, ld,
                          qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale, order,
-                         static_cast<uint16_t*>(out));
+                         static_cast<uint16_t*>(out), 0, nullptr);
     };
-    if (D == 128) args(extend_bf16_kernel<128>);
-    else args(extend_bf16_kernel<64>);
+    if (D == 128) args(extend_bf16_kernel<128, false>);
+    else args(extend_bf16_kernel<64, false>);
     return hip_check("rs_extend_attention");
   }
   if (dtype == RS_DTYPE_F32) {
