@@ -437,7 +437,43 @@ def extra_configs():
         res[str(cfg)] = d
         del st
         torch.cuda.empty_cache()
+    print("[bench] extra: draft-tree verify", file=sys.stderr, flush=True)
+    res["verify"] = verify_extra(flush)
+    torch.cuda.empty_cache()
     return res
+
+
+def verify_extra(flush, B=256, prefix=32768, n=16, Hq=64, Hkv=8, D=128, seed=1009):
+    """Draft-tree verify at the size the pages price the full mask at (256 requests, 32k
+    context, 16 verify tokens): seeded random draft trees and bf16 K/V/Q, each request's
+    context in its own run of slots, inputs resident.  HBM-bound on the unique KV bytes."""
+    import torch
+    import radix_tree_prefix_amd as rs
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    S = B * (prefix + n)
+    kp = torch.randn((S, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    vp = torch.randn((S, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    q = torch.randn((B * n, Hq, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    table = torch.arange(S, dtype=torch.int32, device="cuda").view(B, prefix + n)
+    parents = np.stack([np.array([-1] + [int(rng.integers(0, i)) for i in range(1, n)], np.int32)
+                        for _ in range(B)])
+    mask, pos, _nt, _ns = rs.draft_tree_build(parents, np.full(B, prefix, np.int32))
+    mask_dev = torch.from_numpy(mask.view(np.int64)).cuda()
+    prefix_dev = torch.full((B,), prefix, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    run = lambda: rs.tree_verify_attention(q, kp, vp, table, prefix_dev, mask_dev, 1 / np.sqrt(D), out=out)
+    med, _ = time_fn(run, 20, 3, flush)
+    ub = S * 2 * Hkv * D * 2
+    depth1 = (pos - prefix + 1).astype(np.int64)          # keys seen among the verify tokens
+    flops = int(((prefix + depth1).sum()) * Hq * 4 * D)
+    return {"workload": f"draft-tree verify ({B} x {prefix:,} cached + {n} verify tokens, random trees, bf16, "
+                        f"GQA {Hq}/{Hkv}, d{D})",
+            "verify_us": round(med * 1e3, 2), "unique_kv_bytes": ub,
+            "hbm_gbs_unique": round(ub / (med / 1e3) / 1e9, 1),
+            "hbm_frac": round(ub / (med / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / (med / 1e3) / 1e12, 2),
+            "tokens_per_s": round(B * n / (med / 1e3), 1)}
 
 
 if __name__ == "__main__":
