@@ -98,8 +98,13 @@ const char* rs_version(void);
 
 /* ------------------------------------------------------------------ tree [T][B][L] */
 
-/* New empty tree over pool slots 0..pool_slots-1, all free.  page_size must be 1
- * (token-granular; children keyed on their first token [T]).  NULL on failure. */
+/* New empty tree over pool slots 0..pool_slots-1, all free.  page_size >= 1 must divide
+ * pool_slots.  page_size 1: token-granular, children keyed on their first token [T].
+ * page_size ps > 1 [T "A tree, not a map", the details from the source]: keys are
+ * truncated to whole pages, a match is rounded down to a page, children are keyed on
+ * their first page (siblings may share a first token), and slots come in whole pages
+ * (page p = slots p*ps .. p*ps+ps-1; position j of a sequence sits at offset j % ps of
+ * its page).  NULL on failure. */
 rs_tree* rs_tree_create(int64_t pool_slots, int32_t page_size);
 void rs_tree_destroy(rs_tree* t);
 
@@ -109,6 +114,7 @@ void rs_tree_destroy(rs_tree* t);
  * last_access; the lower part keeps its id) [T].  Every node visited gets the current
  * clock tick.  Writes the matched slots to out_slots (host, capacity >= n), their count
  * to *out_len and the node the match ends at to *out_node (0 = root, empty match). */
+/* With pages the match is a whole number of pages. */
 int rs_match_prefix(rs_tree* t, const int32_t* tokens, int64_t n,
                     int32_t* out_slots, int64_t* out_len, int64_t* out_node);
 
@@ -120,17 +126,22 @@ int rs_dec_lock_ref(rs_tree* t, int64_t node);
 
 /* n free slots, lowest ids first, ascending, into out_slots (host).  When fewer than
  * n are free, first evicts (n - free) tokens; if still short, RS_E_NOSPACE: nothing is
- * allocated, and what was evicted stays evicted [L "Worked example"]. */
+ * allocated, and what was evicted stays evicted [L "Worked example"].  With pages: the
+ * ceil(n/ps) lowest free pages are taken (the end of the last one belongs to the caller
+ * too) and the first n of their slots written, page by page; eviction counts pages. */
 int rs_alloc_slots(rs_tree* t, int64_t n, int32_t* out_slots);
 
-/* Return slots that were allocated and never inserted.  Freeing a free slot is RS_E_INVAL. */
+/* Return slots that were allocated and never inserted.  Freeing a free slot is RS_E_INVAL.
+ * With pages the pages holding the slots are freed (a page named twice, once). */
 int rs_free_slots(rs_tree* t, const int32_t* slots, int64_t n);
 
 /* Insert tokens[0..n) with slots[0..n) (host, in/out) [L step 4].  Splits at the
  * divergence point like match.  Positions already in the tree keep the tree's slots:
  * a caller slot that differs is freed and overwritten with the tree's.  The rest,
  * slots[prefix..n), is adopted by one new leaf.  Returns the count already present
- * in *out_prefix_len and the node the sequence ends at in *out_node. */
+ * in *out_prefix_len and the node the sequence ends at in *out_node.  With pages only
+ * the whole pages of tokens[0..n) are inserted (the caller keeps the rest), and their
+ * slots must be whole pages aligned with the positions (RS_E_INVAL otherwise). */
 int rs_insert(rs_tree* t, const int32_t* tokens, int32_t* slots, int64_t n,
               int64_t* out_prefix_len, int64_t* out_node);
 
@@ -146,7 +157,11 @@ int64_t rs_evict(rs_tree* t, int64_t num_tokens);
  * out_row (host, capacity cached + n_new) receives the request's index-table row.
  * *out_node = the locked node; *out_matched = tokens matched (positions
  * matched..cached+n_new-1 need their KV written).  On RS_E_NOSPACE the request holds
- * no lock and no slots; tokens it already inserted stay cached. */
+ * no lock and no slots; tokens it already inserted stay cached.  With pages the locked
+ * node covers the whole pages of the cached tokens; the request keeps its last page when
+ * the cached tokens end inside it (their slots are in out_row), the new tokens continue
+ * that page before taking fresh pages, and the caller frees the last page with
+ * rs_free_slots when the request ends. */
 int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new,
              int32_t* out_row, int64_t* out_node, int64_t* out_matched);
 
@@ -190,7 +205,8 @@ int rs_schedule(const rs_tree* t, const int32_t* tokens, const int64_t* offsets,
 /* Segments of a decode batch from the tree [L "How the runtime and frontend work
  * together": forked requests reach the runtime as near-identical requests and their
  * common part is computed once].  Request b (table row b) holds a lock on nodes[b],
- * whose root path covers positions 0..cached_lens[b]-1; seq_lens[b] >= cached_lens[b]
+ * whose root path covers positions 0..cached_lens[b]-1 (with pages: the whole pages of
+ * its cached tokens, which is what rs_admit locks); seq_lens[b] >= cached_lens[b]
  * is its context including the new token(s).  A tree node on the paths of >= 2
  * requests becomes a shared segment (a parent-child chain with one request set is one
  * segment); the rest of each request, up to seq_lens[b], is its unique tail.  Segments

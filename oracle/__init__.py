@@ -8,7 +8,7 @@ radix_tree_prefix_amd/ and imports nothing from it.
 """
 from .tree import RadixTree, NoSpace, Stale, common_prefix_len  # noqa: F401
 from .attention import attend, merge_states  # noqa: F401
-from .admit import (admit, release, admit_history, admit_batch,  # noqa: F401
+from .admit import (admit, release, release_tail, admit_history, admit_batch,  # noqa: F401
                     prefill_no_sharing, prefill_sequential, prefill_fixed_prefix)
 from .schedule import schedule, peek_match  # noqa: F401
 from . import speculative  # noqa: F401

@@ -13,6 +13,10 @@ Batch admission of one request with ``cached`` tokens to (re)establish and
 slots for the unmatched cached part (re-prefill after an eviction); insert
 the cached part and move the lock to the node it ends at; allocate the new
 tokens' slots.  The request's index-table row is the ``cached + new`` slots.
+
+With pages (page_size ps > 1) the tree holds whole pages only: the cached part's
+slots come as whole pages, the last of which the request keeps when the cached
+tokens end inside it; its new tokens continue that page before taking fresh pages.
 """
 from __future__ import annotations
 
@@ -34,21 +38,40 @@ def admit(tree: RadixTree, tokens, cached: int, new: int):
     tree.inc_lock_ref(node)
     row = np.empty(cached + new, dtype=np.int32)
     row[:m] = got
+    ps = tree.ps
+    tail = 0                        # slots left in the request's last page after `cached`
     try:
         if cached > m:
             row[m:cached] = tree.alloc(cached - m)
+            if cached % ps:
+                tail = ps - cached % ps
             _p, node2, fixed = tree.insert(tokens[:cached], row[:cached])
             row[:cached] = fixed
             tree.inc_lock_ref(node2)
             tree.dec_lock_ref(node)
             node = node2
         if new:
-            row[cached:] = tree.alloc(new)
+            k = min(new, tail)
+            if k:
+                row[cached:cached + k] = row[cached - 1] + 1 + np.arange(k)
+            if new > k:
+                row[cached + k:] = tree.alloc(new - k)
     except NoSpace:
-        # the request waits: drop its lock; whatever was inserted stays cached
+        # the request waits: drop its lock and its own last page; whatever was
+        # inserted stays cached
+        if tail:
+            tree.free_slots(row[cached - 1:cached])
         tree.dec_lock_ref(node)
         raise
     return row, node, m
+
+
+def release_tail(tree: RadixTree, row):
+    """Free the request's own last page: the positions past its last whole page, which the
+    tree never holds (nothing to do with page size 1)."""
+    n_al = len(row) // tree.ps * tree.ps
+    if n_al < len(row):
+        tree.free_slots(row[n_al:n_al + 1])
 
 
 def release(tree: RadixTree, tokens, row, node):

@@ -34,9 +34,9 @@ def peek_match(tree, tokens):
     """(matched length, deepest node fully matched) without changing the tree."""
     tokens = np.asarray(tokens, dtype=np.int32)
     node, pos = tree.root, 0
-    while pos < len(tokens) and int(tokens[pos]) in node.children:
-        child = node.children[int(tokens[pos])]
-        k = common_prefix_len(child.key, tokens[pos:])
+    while tree._has_page(tokens, pos) and tree._ckey(tokens, pos) in node.children:
+        child = node.children[tree._ckey(tokens, pos)]
+        k = common_prefix_len(child.key, tokens[pos:]) // tree.ps * tree.ps
         pos += k
         if k < len(child.key):
             break
@@ -71,7 +71,7 @@ def _dfs_weight(tree, nodes):
     out = []
 
     def visit(nd):
-        kids = [(weight(c), int(c.key[0]), c) for c in nd.children.values()]
+        kids = [(weight(c), tree._ckey(c.key, 0), c) for c in nd.children.values()]
         kids = [k for k in kids if k[0] > 0]
         kids.sort(key=lambda k: (-k[0], k[1]))
         for _, _, c in kids:

@@ -20,8 +20,17 @@ What it follows (pages as given, sections named):
   and "Worked example, step by step" (least recently used unlocked leaf goes
   first, a node is evicted whole, nothing evictable means the request waits).
 
+Paged variant, same page ("SGLang: the tree, ...", section "A tree, not a
+map", the two details from the source): with page_size > 1 every key is
+truncated to a multiple of the page size, a match is rounded down to one, and
+a node's children are keyed on their first page (all page_size tokens).
+Readings for it: slots come in whole pages (page p holds slots p*ps ..
+p*ps+ps-1, lowest free pages first, a page is freed whole); a request's
+tokens that do not fill a page stay with the request (its last page, which
+later tokens continue) and are not inserted.
+
 Readings where the pages are silent (each listed in the design notes):
-page_size 1; a logical clock that ticks once per match/insert call and
+page_size 1 unless asked; a logical clock that ticks once per match/insert call and
 stamps every node the call visits; heap key (priority, last_access, node id)
 with priority 0; splits in both match and insert, the new upper node taking
 a fresh id and the lower node's lock_ref and last_access; lowest-free-first
@@ -65,8 +74,10 @@ def common_prefix_len(a: np.ndarray, b: np.ndarray) -> int:
 
 
 class RadixTree:
-    def __init__(self, pool_slots: int):
+    def __init__(self, pool_slots: int, page_size: int = 1):
         self.pool_slots = int(pool_slots)
+        self.ps = int(page_size)
+        assert self.ps >= 1 and self.pool_slots % self.ps == 0
         self.root = Node(0, [], [], None)
         self.nodes = {0: self.root}
         self.next_id = 1
@@ -88,17 +99,27 @@ class RadixTree:
         self.next_id += 1
         return i
 
+    def _ckey(self, tokens, pos):
+        """Child key of the edge starting at tokens[pos]: its first token (page size 1)
+        or its first page."""
+        if self.ps == 1:
+            return int(tokens[pos])
+        return tuple(int(x) for x in tokens[pos:pos + self.ps])
+
+    def _has_page(self, tokens, pos):
+        return pos + self.ps <= len(tokens)
+
     def _split(self, child: Node, k: int) -> Node:
         """Cut child's edge after k tokens; the new upper node is returned."""
         upper = Node(self._new_id(), child.key[:k], child.value[:k], child.parent)
         upper.lock_ref = child.lock_ref
         upper.last_access = child.last_access
         upper.priority = child.priority
-        upper.parent.children[int(child.key[0])] = upper
+        upper.parent.children[self._ckey(child.key, 0)] = upper
         child.key = child.key[k:]
         child.value = child.value[k:]
         child.parent = upper
-        upper.children[int(child.key[0])] = child
+        upper.children[self._ckey(child.key, 0)] = child
         self.nodes[upper.id] = upper
         return upper
 
@@ -108,10 +129,10 @@ class RadixTree:
         tokens = np.asarray(tokens, dtype=np.int32)
         self.clock += 1
         node, pos, got = self.root, 0, []
-        while pos < len(tokens) and int(tokens[pos]) in node.children:
-            child = node.children[int(tokens[pos])]
+        while self._has_page(tokens, pos) and self._ckey(tokens, pos) in node.children:
+            child = node.children[self._ckey(tokens, pos)]
             child.last_access = self.clock
-            k = common_prefix_len(child.key, tokens[pos:])
+            k = common_prefix_len(child.key, tokens[pos:]) // self.ps * self.ps
             if k < len(child.key):
                 child = self._split(child, k)
             got.append(child.value)
@@ -131,12 +152,19 @@ class RadixTree:
         tokens = np.asarray(tokens, dtype=np.int32)
         slots = np.array(slots, dtype=np.int32, copy=True)
         assert len(tokens) == len(slots)
+        n = len(tokens) // self.ps * self.ps          # whole pages only
+        tokens = tokens[:n]
+        # slots come in whole pages, aligned with the positions: slot of position j is
+        # page * ps + j % ps, one page per group of ps positions
+        pg = slots[:n].reshape(-1, self.ps) if n else np.zeros((0, self.ps), np.int32)
+        assert (pg[:, :1] % self.ps == 0).all() and (pg == pg[:, :1] + np.arange(self.ps)).all(), \
+            "slots are not whole pages"
         self.clock += 1
         node, pos = self.root, 0
-        while pos < len(tokens) and int(tokens[pos]) in node.children:
-            child = node.children[int(tokens[pos])]
+        while self._has_page(tokens, pos) and self._ckey(tokens, pos) in node.children:
+            child = node.children[self._ckey(tokens, pos)]
             child.last_access = self.clock
-            k = common_prefix_len(child.key, tokens[pos:])
+            k = common_prefix_len(child.key, tokens[pos:]) // self.ps * self.ps
             if k < len(child.key):
                 child = self._split(child, k)
             seg = slots[pos:pos + k]
@@ -147,10 +175,10 @@ class RadixTree:
             pos += k
             node = child
         prefix = pos
-        if pos < len(tokens):
-            leaf = Node(self._new_id(), tokens[pos:], slots[pos:], node)
+        if pos < n:
+            leaf = Node(self._new_id(), tokens[pos:n], slots[pos:n], node)
             leaf.last_access = self.clock
-            node.children[int(tokens[pos])] = leaf
+            node.children[self._ckey(tokens, pos)] = leaf
             self.nodes[leaf.id] = leaf
             self.evictable += len(leaf.key)
             node = leaf
@@ -179,9 +207,12 @@ class RadixTree:
 
     # ---------------------------------------------------------------- slots
     def _free(self, slots):
-        s = np.asarray(slots, dtype=np.int64)
-        assert not self.free[s].any(), "double free"
-        self.free[s] = True
+        """Free the pages that hold these slots (each page whole)."""
+        pages = np.unique(np.asarray(slots, dtype=np.int64) // self.ps)
+        first = pages * self.ps
+        assert not self.free[first].any(), "double free"
+        for p in pages:
+            self.free[p * self.ps:(p + 1) * self.ps] = True
 
     def free_slots(self, slots):
         self._free(slots)
@@ -190,16 +221,19 @@ class RadixTree:
         return int(self.free.sum())
 
     def alloc(self, n: int) -> np.ndarray:
-        """n free slots, lowest ids first; evicts to fit; NoSpace if it cannot."""
+        """n slots from the lowest free whole pages (ceil(n/ps) pages, page-major); evicts to
+        fit; NoSpace if it cannot.  The unused end of the last page belongs to the caller too."""
         n = int(n)
+        need = -(-n // self.ps) * self.ps
         have = self.num_free()
-        if have < n:
-            self.evict(n - have)
-            if self.num_free() < n:
+        if have < need:
+            self.evict(need - have)
+            if self.num_free() < need:
                 raise NoSpace(n)
-        got = np.flatnonzero(self.free)[:n]
+        pages = np.flatnonzero(self.free[::self.ps])[:need // self.ps]
+        got = (pages[:, None] * self.ps + np.arange(self.ps)[None, :]).reshape(-1)
         self.free[got] = False
-        return got.astype(np.int32)
+        return got[:n].astype(np.int32)
 
     # ---------------------------------------------------------------- evict
     def _evictable_leaves(self):
@@ -219,7 +253,7 @@ class RadixTree:
             freed += len(x.value)
             self.evictable -= len(x.key)
             parent = x.parent
-            del parent.children[int(x.key[0])]
+            del parent.children[self._ckey(x.key, 0)]
             del self.nodes[nid]
             if parent is not self.root and not parent.children and parent.lock_ref == 0:
                 heapq.heappush(heap, (parent.priority, parent.last_access, parent.id))
@@ -257,7 +291,7 @@ class RadixTree:
         lines = []
 
         def walk(nd, depth):
-            for ft in sorted(nd.children):
+            for ft in sorted(nd.children):            # first tokens, or first pages as tuples
                 c = nd.children[ft]
                 lines.append("%d %d %d %d %d | %s | %s" % (
                     depth, c.id, c.lock_ref, c.last_access, len(c.key),

@@ -26,33 +26,41 @@ struct Node {
   std::vector<int32_t> key;     // token run on the edge into this node
   std::vector<int32_t> value;   // one pool slot per key token
   Node* parent = nullptr;
-  std::unordered_map<int32_t, Node*> children;  // keyed on the child's first token
+  // keyed on the child's first token; with pages > 1 token, siblings may share it and
+  // differ later in their first page (the page is the key)
+  std::unordered_multimap<int32_t, Node*> children;
   int32_t lock_ref = 0;
   uint64_t last_access = 0;
   int64_t priority = 0;
 };
 
-// Lowest-free-first slot allocator over a bitmap (1 = free) with a word hint.
+// Lowest-free-first allocator of pages of ps slots (page p = slots p*ps .. p*ps+ps-1)
+// over a slot bitmap (1 = free; a page's bits always agree) with a word hint.
 class SlotAllocator {
  public:
-  explicit SlotAllocator(int64_t n);
+  SlotAllocator(int64_t n, int32_t ps);
   int64_t capacity() const { return n_; }
-  int64_t num_free() const { return nfree_; }
-  // Takes the k lowest free slots; caller checked k <= num_free().
+  int64_t num_free() const { return nfree_; }     // slots (whole free pages)
+  int32_t page() const { return ps_; }
+  // Takes the ceil(k/ps) lowest free pages and writes their first k slots, page-major;
+  // caller checked ceil(k/ps)*ps <= num_free().
   void take(int64_t k, int32_t* out);
-  // Returns false (and changes nothing) if any slot is out of range or already free.
+  // Frees the pages that hold these slots (a page named twice is freed once).  Returns
+  // false (and changes nothing) if a slot is out of range or its page is already free.
   bool give_back(const int32_t* s, int64_t k);
   bool is_free(int32_t s) const { return (bits_[s >> 6] >> (s & 63)) & 1ull; }
 
  private:
+  void set_page(int64_t p0, bool free_);
   int64_t n_, nfree_, hint_;
+  int32_t ps_;
   std::vector<uint64_t> bits_;
 };
 
 }  // namespace rs
 
 struct rs_tree {
-  explicit rs_tree(int64_t pool_slots);
+  rs_tree(int64_t pool_slots, int32_t page_size);
 
   rs::Node root;
   std::unordered_map<int64_t, std::unique_ptr<rs::Node>> nodes;   // id -> node (root excluded)
@@ -64,6 +72,11 @@ struct rs_tree {
 
   rs::Node* find(int64_t id);                      // nullptr if stale; root for 0
   const rs::Node* find(int64_t id) const;
+  int32_t ps;                                       // page size (tokens per child key and slot page)
+  // the child of n whose first page is page[0..ps) (nullptr if none)
+  rs::Node* child_at(const rs::Node* n, const int32_t* page) const;
+  void link(rs::Node* parent, rs::Node* c);
+  void unlink(rs::Node* parent, rs::Node* c);
   rs::Node* split(rs::Node* child, int64_t k);      // returns the new upper node
   int64_t match(const int32_t* tok, int64_t n, int32_t* out, rs::Node** end);
   // returns prefix length; slots in/out; frees differing caller slots

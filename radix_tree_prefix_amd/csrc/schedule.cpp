@@ -22,7 +22,8 @@
 // split, no clock tick); ties keep arrival order; a request hangs off the deepest node
 // whose whole root path its tokens match; a node's own requests come after its
 // subtrees (the deeper matches first, cold requests last), children of equal weight
-// in ascending first-token order.
+// in ascending order of their first page (first token at page size 1).  With pages a
+// match is rounded down to a page, as the tree's own match is.
 
 #include <algorithm>
 #include <unordered_map>
@@ -39,12 +40,12 @@ using rs::Node;
 int64_t peek(const rs_tree* t, const int32_t* tok, int64_t n, const Node** deepest) {
   const Node* node = &t->root;
   int64_t pos = 0;
-  while (pos < n) {
-    auto it = node->children.find(tok[pos]);
-    if (it == node->children.end()) break;
-    const Node* c = it->second;
+  const int32_t ps = t->ps;
+  while (pos + ps <= n) {                 // whole pages only
+    const Node* c = t->child_at(node, tok + pos);
+    if (!c) break;
     const int64_t len = int64_t(c->key.size());
-    const int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos));
+    const int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos)) / ps * ps;
     pos += k;
     if (k < len) break;
     node = c;
@@ -106,7 +107,9 @@ void dfs_weight(const rs_tree* t, const std::vector<const Node*>& at, int32_t n,
   for (auto& kv : kids)
     std::sort(kv.second.begin(), kv.second.end(), [&](const Node* a, const Node* b) {
       const int64_t wa = weight[a], wb = weight[b];
-      return wa != wb ? wa > wb : a->key[0] < b->key[0];
+      if (wa != wb) return wa > wb;
+      return std::lexicographical_compare(a->key.begin(), a->key.begin() + t->ps, b->key.begin(),
+                                          b->key.begin() + t->ps);
     });
   // post-order walk with an explicit stack: (node, next child index)
   int32_t k = 0;

@@ -2,7 +2,10 @@
 //
 // Follows "SGLang: the tree, and the language nobody remembers"
 // (ai.thesatyajit.com), section "A tree, not a map": nodes hold a token run,
-// one KV slot per token, children keyed on the first token (page size 1),
+// one KV slot per token, children keyed on the first token (page size 1) or on the
+// first page (larger pages: keys truncated to whole pages, matches rounded down to a
+// page, slots allocated and freed in whole pages, from the same section's details of
+// the source),
 // lock_ref, last access and priority; a node splits at the divergence point;
 // lock_ref changes move a node's tokens between the evictable and protected
 // totals on its 0<->1 edge; eviction pops unlocked leaves off a heap and
@@ -60,38 +63,67 @@ int64_t diverge(const int32_t* a, const int32_t* b, int64_t n) {
   return n;
 }
 
-SlotAllocator::SlotAllocator(int64_t n) : n_(n), nfree_(n), hint_(0), bits_((n + 63) / 64, ~0ull) {
+SlotAllocator::SlotAllocator(int64_t n, int32_t ps)
+    : n_(n), nfree_(n), hint_(0), ps_(ps), bits_((n + 63) / 64, ~0ull) {
   if (n & 63) bits_.back() = (1ull << (n & 63)) - 1;
+}
+
+void SlotAllocator::set_page(int64_t p0, bool free_) {
+  for (int64_t x = p0; x < p0 + ps_; ++x) {
+    if (free_) bits_[x >> 6] |= 1ull << (x & 63);
+    else bits_[x >> 6] &= ~(1ull << (x & 63));
+  }
 }
 
 void SlotAllocator::take(int64_t k, int32_t* out) {
   int64_t got = 0, w = hint_;
-  while (got < k) {
-    uint64_t b = bits_[w];
-    while (b && got < k) {
-      int tz = __builtin_ctzll(b);
-      out[got++] = int32_t(w * 64 + tz);
-      b &= b - 1;
+  if (ps_ == 1) {
+    while (got < k) {
+      uint64_t b = bits_[w];
+      while (b && got < k) {
+        int tz = __builtin_ctzll(b);
+        out[got++] = int32_t(w * 64 + tz);
+        b &= b - 1;
+      }
+      bits_[w] = b;
+      if (!b) ++w;
     }
-    bits_[w] = b;
-    if (!b) ++w;
+    hint_ = w;
+    nfree_ -= k;
+    return;
+  }
+  const int64_t pages = (k + ps_ - 1) / ps_;
+  for (int64_t taken = 0; taken < pages;) {
+    uint64_t b = bits_[w];
+    if (!b) { ++w; continue; }
+    const int64_t p0 = w * 64 + __builtin_ctzll(b);   // the lowest free slot starts a free page
+    set_page(p0, false);
+    for (int64_t i = 0; i < ps_ && got < k; ++i) out[got++] = int32_t(p0 + i);
+    ++taken;
   }
   hint_ = w;
-  nfree_ -= k;
+  nfree_ -= pages * ps_;
 }
 
 bool SlotAllocator::give_back(const int32_t* s, int64_t k) {
+  std::vector<int64_t> freed;          // page starts freed by this call
   for (int64_t i = 0; i < k; ++i) {
-    int32_t x = s[i];
-    bool bad = x < 0 || x >= n_ || is_free(x);
+    const int32_t x = s[i];
+    const int64_t p0 = x < 0 ? -1 : int64_t(x) - int64_t(x) % ps_;
+    bool bad = x < 0 || x >= n_;
+    if (!bad && is_free(int32_t(p0))) {
+      bad = std::find(freed.begin(), freed.end(), p0) == freed.end();   // free before this call
+      if (!bad) continue;
+    }
     if (bad) {
-      for (int64_t j = 0; j < i; ++j) bits_[s[j] >> 6] &= ~(1ull << (s[j] & 63));
+      for (int64_t q : freed) set_page(q, false);
       return false;
     }
-    bits_[x >> 6] |= 1ull << (x & 63);
+    set_page(p0, true);
+    freed.push_back(p0);
   }
-  for (int64_t i = 0; i < k; ++i) hint_ = std::min<int64_t>(hint_, s[i] >> 6);
-  nfree_ += k;
+  for (int64_t q : freed) hint_ = std::min<int64_t>(hint_, q >> 6);
+  nfree_ += int64_t(freed.size()) * ps_;
   return true;
 }
 
@@ -99,7 +131,25 @@ bool SlotAllocator::give_back(const int32_t* s, int64_t k) {
 
 using rs::Node;
 
-rs_tree::rs_tree(int64_t pool_slots) : alloc(pool_slots) { root.id = 0; }
+rs_tree::rs_tree(int64_t pool_slots, int32_t page_size) : alloc(pool_slots, page_size), ps(page_size) { root.id = 0; }
+
+Node* rs_tree::child_at(const Node* n, const int32_t* page) const {
+  auto r = n->children.equal_range(page[0]);
+  for (auto it = r.first; it != r.second; ++it)
+    if (ps == 1 || std::memcmp(it->second->key.data(), page, size_t(ps) * 4) == 0) return it->second;
+  return nullptr;
+}
+
+void rs_tree::link(Node* parent, Node* c) { parent->children.emplace(c->key[0], c); }
+
+void rs_tree::unlink(Node* parent, Node* c) {
+  auto r = parent->children.equal_range(c->key[0]);
+  for (auto it = r.first; it != r.second; ++it)
+    if (it->second == c) {
+      parent->children.erase(it);
+      return;
+    }
+}
 
 Node* rs_tree::find(int64_t id) {
   if (id == 0) return &root;
@@ -122,11 +172,12 @@ Node* rs_tree::split(Node* child, int64_t k) {
   u->lock_ref = child->lock_ref;
   u->last_access = child->last_access;
   u->priority = child->priority;
-  u->parent->children[child->key[0]] = u;
+  unlink(u->parent, child);
+  link(u->parent, u);
   child->key.erase(child->key.begin(), child->key.begin() + k);
   child->value.erase(child->value.begin(), child->value.begin() + k);
   child->parent = u;
-  u->children[child->key[0]] = child;
+  link(u, child);
   nodes.emplace(u->id, std::move(up));
   return u;
 }
@@ -136,13 +187,12 @@ int64_t rs_tree::match(const int32_t* tok, int64_t n, int32_t* out, Node** end) 
   ++match_calls;
   Node* node = &root;
   int64_t pos = 0;
-  while (pos < n) {
-    auto it = node->children.find(tok[pos]);
-    if (it == node->children.end()) break;
-    Node* c = it->second;
+  while (pos + ps <= n) {                 // whole pages only
+    Node* c = child_at(node, tok + pos);
+    if (!c) break;
     c->last_access = clock;
     int64_t len = int64_t(c->key.size());
-    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos));
+    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos)) / ps * ps;
     if (k < len) c = split(c, k);
     if (out) std::memcpy(out + pos, c->value.data(), size_t(k) * 4);
     pos += k;
@@ -154,30 +204,35 @@ int64_t rs_tree::match(const int32_t* tok, int64_t n, int32_t* out, Node** end) 
 }
 
 int rs_tree::insert(const int32_t* tok, int32_t* slots, int64_t n, int64_t* prefix, Node** end) {
-  for (int64_t i = 0; i < n; ++i)
+  n = n / ps * ps;                        // whole pages only; the caller keeps the rest
+  for (int64_t i = 0; i < n; ++i) {
     if (slots[i] < 0 || slots[i] >= alloc.capacity() || alloc.is_free(slots[i]))
       return rs::fail(RS_E_INVAL, "rs_insert: slot " + std::to_string(slots[i]) + " at position " +
                                       std::to_string(i) + " is out of range or not allocated");
+    // with pages: position i's slot is page * ps + i % ps, one page per ps positions
+    if (ps > 1 && (i % ps == 0 ? slots[i] % ps != 0 : slots[i] != slots[i - 1] + 1))
+      return rs::fail(RS_E_INVAL, "rs_insert: slots are not whole pages aligned with the positions (position " +
+                                      std::to_string(i) + ")");
+  }
   ++clock;
   ++insert_calls;
   Node* node = &root;
   int64_t pos = 0;
   int rc = RS_OK;
-  while (pos < n) {
-    auto it = node->children.find(tok[pos]);
-    if (it == node->children.end()) break;
-    Node* c = it->second;
+  std::vector<int32_t> differ;
+  while (pos + ps <= n) {
+    Node* c = child_at(node, tok + pos);
+    if (!c) break;
     c->last_access = clock;
     int64_t len = int64_t(c->key.size());
-    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos));
+    int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos)) / ps * ps;
     if (k < len) c = split(c, k);
-    for (int64_t i = 0; i < k; ++i) {
-      int32_t& s = slots[pos + i];
-      if (s != c->value[i]) {
-        if (!alloc.give_back(&s, 1)) rc = rs::fail(RS_E_INVAL, "rs_insert: duplicate caller slot");
-        s = c->value[i];
-      }
-    }
+    differ.clear();
+    for (int64_t i = 0; i < k; ++i)
+      if (slots[pos + i] != c->value[i]) differ.push_back(slots[pos + i]);
+    if (!differ.empty() && !alloc.give_back(differ.data(), int64_t(differ.size())))
+      rc = rs::fail(RS_E_INVAL, "rs_insert: duplicate caller slot");
+    for (int64_t i = 0; i < k; ++i) slots[pos + i] = c->value[i];
     pos += k;
     node = c;
   }
@@ -190,7 +245,7 @@ int rs_tree::insert(const int32_t* tok, int32_t* slots, int64_t n, int64_t* pref
     l->value.assign(slots + pos, slots + n);
     l->parent = node;
     l->last_access = clock;
-    node->children[tok[pos]] = l;
+    link(node, l);
     nodes.emplace(l->id, std::move(leaf));
     evictable += n - pos;
     tree_tokens += n - pos;
@@ -241,7 +296,7 @@ int64_t rs_tree::evict(int64_t need) {
     evictable -= len;
     tree_tokens -= len;
     Node* p = x->parent;
-    p->children.erase(x->key[0]);
+    unlink(p, x);
     nodes.erase(id);
     if (p != &root && p->children.empty() && p->lock_ref == 0)
       heap.emplace(p->priority, p->last_access, p->id);
@@ -252,9 +307,10 @@ int64_t rs_tree::evict(int64_t need) {
 
 int rs_tree::alloc_slots(int64_t n, int32_t* out) {
   if (n < 0) return rs::fail(RS_E_INVAL, "rs_alloc_slots: negative count");
-  if (alloc.num_free() < n) {
-    evict(n - alloc.num_free());
-    if (alloc.num_free() < n)
+  const int64_t need = (n + ps - 1) / ps * ps;       // whole pages
+  if (alloc.num_free() < need) {
+    evict(need - alloc.num_free());
+    if (alloc.num_free() < need)
       return rs::fail(RS_E_NOSPACE, "rs_alloc_slots: " + std::to_string(n) + " slots wanted, " +
                                         std::to_string(alloc.num_free()) +
                                         " free after evicting every unlocked leaf");
@@ -291,12 +347,12 @@ rs_tree* rs_tree_create(int64_t pool_slots, int32_t page_size) {
     rs::set_error("rs_tree_create: pool_slots must be in [1, 2^31)");
     return nullptr;
   }
-  if (page_size != 1) {
-    rs::set_error("rs_tree_create: only page_size 1 (token-granular) is implemented");
+  if (page_size < 1 || pool_slots % page_size != 0) {
+    rs::set_error("rs_tree_create: page_size must be >= 1 and divide pool_slots");
     return nullptr;
   }
   try {
-    return new rs_tree(pool_slots);
+    return new rs_tree(pool_slots, page_size);
   } catch (...) {
     rs::set_error("rs_tree_create: out of host memory");
     return nullptr;
@@ -378,12 +434,15 @@ int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new, i
   Node* node = nullptr;
   int64_t m = t->match(tokens, cached, out_row, &node);
   t->lock(node);
+  const int32_t ps = t->ps;
+  int64_t tail = 0;                 // slots left in the request's own last page after `cached`
   if (cached > m) {
     int rc = t->alloc_slots(cached - m, out_row + m);
     if (rc != RS_OK) {
       t->unlock(node);
       return rc;
     }
+    if (cached % ps) tail = ps - cached % ps;
     int64_t prefix = 0;
     Node* node2 = nullptr;
     rc = t->insert(tokens, out_row, cached, &prefix, &node2);
@@ -396,10 +455,16 @@ int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new, i
     node = node2;
   }
   if (n_new) {
-    int rc = t->alloc_slots(n_new, out_row + cached);
-    if (rc != RS_OK) {
-      t->unlock(node);
-      return rc;
+    // the new tokens continue the request's last page, then take fresh pages
+    const int64_t k = std::min(n_new, tail);
+    for (int64_t i = 0; i < k; ++i) out_row[cached + i] = out_row[cached - 1] + 1 + int32_t(i);
+    if (n_new > k) {
+      int rc = t->alloc_slots(n_new - k, out_row + cached + k);
+      if (rc != RS_OK) {
+        if (tail) t->alloc.give_back(out_row + cached - 1, 1);   // the request's own last page
+        t->unlock(node);
+        return rc;
+      }
     }
   }
   *out_node = node->id;
@@ -430,14 +495,17 @@ int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need) {
   RS_GUARD_BEGIN
   std::string s;
   char tmp[96];
-  // explicit stack: (node, depth); children pushed in descending first-token order
+  // explicit stack: (node, depth); children pushed in descending first-page order
   std::vector<std::pair<const Node*, int>> st;
+  const int32_t ps = t->ps;
   auto push_children = [&](const Node* n, int depth) {
-    std::vector<int32_t> keys;
-    keys.reserve(n->children.size());
-    for (auto& kv : n->children) keys.push_back(kv.first);
-    std::sort(keys.begin(), keys.end());
-    for (auto it = keys.rbegin(); it != keys.rend(); ++it) st.emplace_back(n->children.at(*it), depth);
+    std::vector<const Node*> kids;
+    kids.reserve(n->children.size());
+    for (auto& kv : n->children) kids.push_back(kv.second);
+    std::sort(kids.begin(), kids.end(), [&](const Node* a, const Node* b) {
+      return std::lexicographical_compare(a->key.begin(), a->key.begin() + ps, b->key.begin(), b->key.begin() + ps);
+    });
+    for (auto it = kids.rbegin(); it != kids.rend(); ++it) st.emplace_back(*it, depth);
   };
   push_children(&t->root, 0);
   while (!st.empty()) {
