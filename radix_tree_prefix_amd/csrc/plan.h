@@ -12,7 +12,7 @@ constexpr int32_t kPlanHeaderWords = 16;
 constexpr int32_t kItemWords = 8;            // k0, k1, rep_row, n_req, req_off, part_base, -, -
 constexpr int32_t kMaxRowsPerItem = 128;     // 4 waves x 32 query rows
 constexpr int32_t kFlatChunk = 256;          // keys per item in the flat (plan-less) mode
-constexpr int64_t kDecodeItemsTarget = 2048; // items x KV heads the chunk size aims for
+constexpr int64_t kDecodeItemsTarget = 1024; // items x KV heads the chunk size aims for (fewer, longer items pay fewer workgroup start-ups)
 constexpr int64_t kMinChunk = 512;           // >= 8 tiles per item: a work item pays several round trips before it streams
 constexpr int64_t kMaxChunk = 8192;
 
