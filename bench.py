@@ -368,7 +368,7 @@ def main():
     ext_tf = flops / (ext_ms / 1e3) / 1e12 if st.ext else 0.0
     dec_gbs = ub / (dec_ms / 1e3) / 1e9 if st.dec else 0.0
     if st.ext:
-        roof = {"bound": "mfma", "kernel": "extend_bf16_kernel<128>", "achieved": round(ext_tf, 2),
+        roof = {"bound": "mfma", "kernel": "extend_bf16_kernel<128, false>", "achieved": round(ext_tf, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ext_tf / BF16_PEAK_TFLOPS, 4),
                 "traffic": None, "algorithmic_per_launch": flops, "avg_launch_ms": round(ext_ms, 4)}
         tr = measured_traffic(roof["kernel"], args.config)
