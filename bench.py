@@ -440,7 +440,59 @@ def extra_configs():
     print("[bench] extra: draft-tree verify", file=sys.stderr, flush=True)
     res["verify"] = verify_extra(flush)
     torch.cuda.empty_cache()
+    print("[bench] extra: host tier copies", file=sys.stderr, flush=True)
+    res["host_tier"] = host_tier_extra()
+    torch.cuda.empty_cache()
     return res
+
+
+def host_tier_extra(tokens=65536, Hkv=8, D=128, seed=1013):
+    """Two-tier cache: a 64k-token prefix written through to pinned host pools and loaded
+    back, with the pairs the tree hands out (rs_copy_kv over the bus), beside a contiguous
+    copy of the same bytes as the bus's own rate; and the tree calls' host time."""
+    import time
+    import torch
+    import radix_tree_prefix_amd as rs
+    S = H = 2 * tokens
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dk = torch.randn((S, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    dv = torch.randn((S, Hkv, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    hk = rs.host_pool((H, Hkv, D), torch.bfloat16)
+    hv = rs.host_pool((H, Hkv, D), torch.bfloat16)
+    tree = rs.Tree(S)
+    tree.enable_host(H)
+    rng = np.random.default_rng(seed)
+    toks = rng.integers(0, 32000, tokens).astype(np.int32)
+    for i in range(0, tokens, 4096):              # the prefix arrives in 16 chunks: 16 nodes
+        row, node, _m = tree.admit(toks[:i + 4096], i + 4096, 0)
+        tree.dec_lock_ref(node)
+    t0 = time.perf_counter()
+    d, h, tk = tree.write_through(node)
+    t_wt = time.perf_counter() - t0
+    d_dev, h_dev = torch.from_numpy(d).cuda(), torch.from_numpy(h).cuda()
+    d2h = lambda: rs.copy_kv(hk, hv, dk, dv, h_dev, d_dev)
+    med_d2h, _ = time_fn(d2h, 10, 2)
+    tree.commit(tk, True)
+    tree.evict(S)
+    t0 = time.perf_counter()
+    src, dst, tk = tree.load_back(node)
+    t_lb = time.perf_counter() - t0
+    s_dev, t_dev = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
+    h2d = lambda: rs.copy_kv(dk, dv, hk, hv, t_dev, s_dev)
+    med_h2d, _ = time_fn(h2d, 10, 2)
+    tree.commit(tk, True)
+    nbytes = 2 * len(d) * Hkv * D * 2
+    flat_dev = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    flat_host = rs.host_pool((nbytes // 2,), torch.bfloat16)
+    med_cd2h, _ = time_fn(lambda: flat_host.copy_(flat_dev, non_blocking=True), 10, 2)
+    med_ch2d, _ = time_fn(lambda: flat_dev.copy_(flat_host, non_blocking=True), 10, 2)
+    gbs = lambda ms: round(nbytes / (ms / 1e3) / 1e9, 1)
+    return {"workload": f"host tier: {tokens:,}-token prefix in 16 nodes, K+V bf16 GQA {Hkv}x{D} "
+                        f"({nbytes / 2**20:.0f} MiB), pinned host pools",
+            "write_through_us": round(med_d2h * 1e3, 1), "write_through_gbs": gbs(med_d2h),
+            "load_back_us": round(med_h2d * 1e3, 1), "load_back_gbs": gbs(med_h2d),
+            "contiguous_d2h_gbs": gbs(med_cd2h), "contiguous_h2d_gbs": gbs(med_ch2d),
+            "tree_write_through_ms": round(t_wt * 1e3, 3), "tree_load_back_ms": round(t_lb * 1e3, 3)}
 
 
 def verify_extra(flush, B=256, prefix=32768, n=16, Hq=64, Hkv=8, D=128, seed=1009):

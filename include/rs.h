@@ -76,7 +76,10 @@ typedef struct rs_stats_t {
   int64_t matched_total;  /* tokens returned by rs_match_prefix since creation */
   int64_t match_calls;
   int64_t insert_calls;
-  int64_t reserved[5];
+  int64_t host_slots;     /* host tier size (0: off) */
+  int64_t host_tokens;    /* tokens with a host copy */
+  int64_t host_free;      /* free host slots */
+  int64_t reserved[2];
 } rs_stats_t;
 
 typedef struct rs_plan_info_t {
@@ -173,6 +176,53 @@ int rs_stats(const rs_tree* t, rs_stats_t* out);
  * Writes at most cap bytes (NUL-terminated if room) and the full size (excluding
  * the NUL) to *need. */
 int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need);
+
+/* ------------------------------------------------------------------ host tier */
+
+/* A second tier of host_slots slots in host memory [T "What the C++ tree is actually
+ * for": a two-tier cache with asynchronous copies resolved by a later commit; nodes on the
+ * GPU, on the CPU or both].  The library keeps the host slot ids; the caller owns the host
+ * K/V pools ([host_slots][Hkv][D] each, pinned so that rs_copy_kv can reach them) and moves
+ * the rows.  Page size 1 only (RS_E_UNSUPPORTED otherwise); at most once per tree.
+ * With the tier on, device eviction keeps a node that has a finished host copy, on the host
+ * only; rs_match_prefix stops at such nodes; rs_insert over them gives them the caller's
+ * device slots again.  A node is on the host only after its device slots were evicted, and
+ * every node below it is then on the host only too. */
+int rs_host_tier_enable(rs_tree* t, int64_t host_slots);
+
+/* Like rs_match_prefix, continued through nodes that are on the host only (split and
+ * touched the same way): *out_dev_len tokens are on the device (slots in out_dev_slots,
+ * node *out_dev_node), *out_len in total; out_host_slots receives the host slots of
+ * positions *out_dev_len .. *out_len-1, *out_node is the node the match ends at. */
+int rs_match_prefix2(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_dev_slots,
+                     int32_t* out_host_slots, int64_t* out_dev_len, int64_t* out_len,
+                     int64_t* out_dev_node, int64_t* out_node);
+
+/* Write-through: host slots for every node on node's root path that has no host copy (the
+ * path must be on the device), evicting host-only leaves, least recently used first, to
+ * fit (RS_E_NOSPACE if it cannot: what was evicted stays evicted, nothing else changes).  Writes the (device slot, host slot)
+ * pairs to copy, *out_n of them (host arrays of capacity cap), and a ticket; the path stays
+ * locked and the copies count as in flight until rs_commit(ticket). */
+int rs_write_through(rs_tree* t, int64_t node, int64_t cap, int32_t* out_dev_slots,
+                     int32_t* out_host_slots, int64_t* out_n, int64_t* out_ticket);
+
+/* Load back: device slots (rs_alloc_slots rules, evicting to fit; RS_E_NOSPACE: what was
+ * evicted stays evicted, nothing else changes) for every node on node's root path that is on the host only; writes the (host slot,
+ * device slot) pairs to copy and a ticket; the path stays locked until rs_commit(ticket). */
+int rs_load_back(rs_tree* t, int64_t node, int64_t cap, int32_t* out_host_slots,
+                 int32_t* out_dev_slots, int64_t* out_n, int64_t* out_ticket);
+
+/* Resolve a ticket.  A write-through is committed once its copies are done (success != 0)
+ * or abandoned (success == 0: its host slots are freed).  A load back is committed with
+ * success != 0 once its copies have run (RS_E_INVAL otherwise; nothing changes): only the
+ * write-through's commit carries an outcome in the interface the page prints.  Until then its
+ * nodes already hold their device slots, so a match may return them: kernels that read those
+ * rows must be ordered after the copy (same stream, or an event).  The path is unlocked. */
+int rs_commit(rs_tree* t, int64_t ticket, int32_t success);
+
+/* Drop host-only leaves, least (priority, last_access, id) first, until num_tokens host
+ * slots are free; returns the number freed. */
+int64_t rs_evict_host(rs_tree* t, int64_t num_tokens);
 
 /* ------------------------------------------------------------------ scheduling */
 
@@ -305,6 +355,22 @@ int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_po
  * slot and from every src slot at another index; otherwise the result is undefined. */
 int rs_move_kv(void* k_pool, void* v_pool, const int32_t* src_slots, const int32_t* dst_slots,
                int64_t n, int32_t Hkv, int32_t D, int32_t dtype, void* stream);
+
+/* Pinned host memory for the host tier's K/V pools [T "What the C++ tree is actually for"],
+ * mapped for the GPU at its host address (RS_E_UNSUPPORTED if the runtime maps it elsewhere,
+ * RS_E_NOSPACE if it cannot be had).  The caller owns it until rs_host_free. */
+int rs_host_alloc(int64_t bytes, void** out);
+int rs_host_free(void* p);
+
+/* Copy rows between two pools: dst_k[dst_slots[r]] = src_k[src_slots[r]] and the same for V
+ * (r < n; slot arrays device int32; pools [rows][Hkv][D], dst_rows and src_rows rows, 16-byte
+ * aligned).  A pool is device memory, or lies wholly inside a block from rs_host_alloc (the
+ * host tier's copies of rs_write_through / rs_load_back, which the kernel reads or writes over
+ * the bus); any other pointer is refused with RS_E_INVAL before anything runs.  A row whose slot
+ * lies outside its pool is skipped.  Destinations must be distinct. */
+int rs_copy_kv(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int32_t* dst_slots,
+               const int32_t* src_slots, int64_t n, int64_t dst_rows, int64_t src_rows, int32_t Hkv,
+               int32_t D, int32_t dtype, void* stream);
 
 /* Decode attention: one query per request at position seq_lens[b]-1 over positions
  * 0..seq_lens[b]-1 (its own KV stored first) [L "A quick recap"].  q, out: device

@@ -51,12 +51,15 @@ class Stale(Exception):
 
 
 class Node:
-    __slots__ = ("id", "key", "value", "children", "parent", "lock_ref", "last_access", "priority")
+    __slots__ = ("id", "key", "value", "children", "parent", "lock_ref", "last_access", "priority", "host",
+                 "pend")
 
     def __init__(self, nid, key, value, parent):
         self.id = nid
         self.key = np.asarray(key, dtype=np.int32)
-        self.value = np.asarray(value, dtype=np.int32)
+        self.value = np.asarray(value, dtype=np.int32)    # device slots; empty: the node is on the host only
+        self.host = np.zeros(0, np.int32)                  # host slots; empty: no host copy
+        self.pend = 0                                      # ticket of a copy in flight, 0 if none
         self.children = {}          # first token -> Node
         self.parent = parent
         self.lock_ref = 0
@@ -86,6 +89,10 @@ class RadixTree:
         self.evictable = 0
         self.protected = 0
         self.evicted_total = 0
+        self.host_slots = 0                 # host tier off until enable_host
+        self.host_free = np.zeros(0, bool)
+        self.tickets = {}                   # ticket -> (kind, node id locked for it)
+        self.next_ticket = 1
 
     # ---------------------------------------------------------------- helpers
     def _node(self, nid) -> Node:
@@ -115,6 +122,8 @@ class RadixTree:
         upper.lock_ref = child.lock_ref
         upper.last_access = child.last_access
         upper.priority = child.priority
+        upper.host, upper.pend = child.host[:k], child.pend
+        child.host = child.host[k:]
         upper.parent.children[self._ckey(child.key, 0)] = upper
         child.key = child.key[k:]
         child.value = child.value[k:]
@@ -131,6 +140,8 @@ class RadixTree:
         node, pos, got = self.root, 0, []
         while self._has_page(tokens, pos) and self._ckey(tokens, pos) in node.children:
             child = node.children[self._ckey(tokens, pos)]
+            if not len(child.value):        # on the host only: not a device match
+                break
             child.last_access = self.clock
             k = common_prefix_len(child.key, tokens[pos:]) // self.ps * self.ps
             if k < len(child.key):
@@ -168,6 +179,12 @@ class RadixTree:
             if k < len(child.key):
                 child = self._split(child, k)
             seg = slots[pos:pos + k]
+            if not len(child.value):        # on the host only: it takes the caller's device slots
+                child.value = seg.copy()
+                if child.lock_ref > 0:
+                    self.protected += k
+                else:
+                    self.evictable += k
             differ = seg != child.value
             if differ.any():
                 self._free(seg[differ])
@@ -189,8 +206,8 @@ class RadixTree:
         node = self._node(nid)
         while node is not self.root:
             if node.lock_ref == 0:
-                self.evictable -= len(node.key)
-                self.protected += len(node.key)
+                self.evictable -= len(node.value)
+                self.protected += len(node.value)
             node.lock_ref += 1
             node = node.parent
 
@@ -200,8 +217,8 @@ class RadixTree:
             raise ValueError("dec_lock_ref below zero")
         while node is not self.root:
             if node.lock_ref == 1:
-                self.evictable += len(node.key)
-                self.protected -= len(node.key)
+                self.evictable += len(node.value)
+                self.protected -= len(node.value)
             node.lock_ref -= 1
             node = node.parent
 
@@ -236,12 +253,17 @@ class RadixTree:
         return got[:n].astype(np.int32)
 
     # ---------------------------------------------------------------- evict
+    @staticmethod
+    def _device_leaf(nd):
+        """On the device, unlocked, and no child on the device."""
+        return len(nd.value) > 0 and nd.lock_ref == 0 and not any(len(c.value) for c in nd.children.values())
+
     def _evictable_leaves(self):
-        return [nd for nd in self.nodes.values()
-                if nd is not self.root and not nd.children and nd.lock_ref == 0]
+        return [nd for nd in self.nodes.values() if nd is not self.root and self._device_leaf(nd)]
 
     def evict(self, num_tokens: int) -> int:
-        """Evict whole unlocked leaves, least key first, until num_tokens are freed."""
+        """Evict whole unlocked device leaves, least key first, until num_tokens are freed.  A
+        node with a finished host copy stays, on the host only; any other leaves the tree."""
         import heapq
         heap = [(nd.priority, nd.last_access, nd.id) for nd in self._evictable_leaves()]
         heapq.heapify(heap)
@@ -251,14 +273,158 @@ class RadixTree:
             x = self.nodes[nid]
             self._free(x.value)
             freed += len(x.value)
-            self.evictable -= len(x.key)
+            self.evictable -= len(x.value)
             parent = x.parent
-            del parent.children[self._ckey(x.key, 0)]
-            del self.nodes[nid]
-            if parent is not self.root and not parent.children and parent.lock_ref == 0:
+            if len(x.host) and x.pend == 0:
+                x.value = np.zeros(0, np.int32)
+            else:
+                self._drop_subtree(x)       # what is left below is on the host only: it goes too
+                del parent.children[self._ckey(x.key, 0)]
+                del self.nodes[nid]
+            if parent is not self.root and self._device_leaf(parent):
                 heapq.heappush(heap, (parent.priority, parent.last_access, parent.id))
         self.evicted_total += freed
         return freed
+
+    # ---------------------------------------------------------------- host tier
+    # "SGLang: the tree, ..." (ai.thesatyajit.com), "What the C++ tree is actually for": a
+    # second tier in host memory; a match also reports how far it runs on the host, with
+    # a node handle per tier; copies to the host (writing through) and back (loading) are
+    # transactions that a later commit resolves; nodes are on the GPU, on the CPU or both.
+    def enable_host(self, host_slots: int):
+        assert self.ps == 1 and self.host_slots == 0 and host_slots > 0
+        self.host_slots = int(host_slots)
+        self.host_free = np.ones(self.host_slots, bool)
+
+    def _host_leaves(self):
+        return [nd for nd in self.nodes.values()
+                if nd is not self.root and not len(nd.value) and not nd.children and nd.lock_ref == 0
+                and nd.pend == 0]
+
+    def evict_host(self, num_tokens: int) -> int:
+        """Drop host-only leaves, least (priority, last_access, id) first, until num_tokens host
+        slots are freed; a parent left a host-only leaf follows."""
+        import heapq
+        heap = [(nd.priority, nd.last_access, nd.id) for nd in self._host_leaves()]
+        heapq.heapify(heap)
+        freed = 0
+        while freed < num_tokens and heap:
+            _p, _t, nid = heapq.heappop(heap)
+            x = self.nodes[nid]
+            self.host_free[x.host] = True
+            freed += len(x.host)
+            parent = x.parent
+            del parent.children[self._ckey(x.key, 0)]
+            del self.nodes[nid]
+            if (parent is not self.root and not len(parent.value) and not parent.children
+                    and parent.lock_ref == 0 and parent.pend == 0):
+                heapq.heappush(heap, (parent.priority, parent.last_access, parent.id))
+        return freed
+
+    def _drop_subtree(self, x):
+        for c in list(x.children.values()):
+            assert not len(c.value) and c.lock_ref == 0 and c.pend == 0
+            self._drop_subtree(c)
+            self.host_free[c.host] = True
+            del self.nodes[c.id]
+        x.children.clear()
+
+    def _alloc_host(self, n):
+        have = int(self.host_free.sum())
+        if have < n:
+            self.evict_host(n - have)
+            if int(self.host_free.sum()) < n:
+                raise NoSpace(n)
+        got = np.flatnonzero(self.host_free)[:n]
+        self.host_free[got] = False
+        return got.astype(np.int32)
+
+    def match2(self, tokens):
+        """(device slots, host slots, device length, total length, device node, last node): the
+        device match as match_prefix, continued through nodes that are on the host only."""
+        tokens = np.asarray(tokens, dtype=np.int32)
+        self.clock += 1
+        node, pos, dev, host = self.root, 0, [], []
+        dev_node, dev_len = self.root, 0
+        while pos < len(tokens) and int(tokens[pos]) in node.children:
+            child = node.children[int(tokens[pos])]
+            child.last_access = self.clock
+            k = common_prefix_len(child.key, tokens[pos:])
+            if k < len(child.key):
+                child = self._split(child, k)
+            if len(child.value) and dev_len == pos:
+                dev.append(child.value)
+                dev_node, dev_len = child, pos + k
+            else:
+                host.append(child.host)
+            pos += k
+            node = child
+        cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int32)
+        return cat(dev), cat(host), dev_len, pos, dev_node.id, node.id
+
+    def write_through(self, nid):
+        """Host copies for the device nodes on nid's root path that have none: returns (device
+        slots, host slots, ticket); the path stays locked until commit."""
+        path = self.path(nid)
+        assert all(len(nd.value) for nd in path), "write-through of a node not on the device"
+        todo = [nd for nd in path if not len(nd.host) and nd.pend == 0]
+        need = sum(len(nd.key) for nd in todo)
+        got = self._alloc_host(need)
+        t = self.next_ticket
+        self.next_ticket += 1
+        src, dst, o = [], [], 0
+        for nd in todo:
+            nd.host = got[o:o + len(nd.key)]
+            nd.pend = t
+            o += len(nd.key)
+            src.append(nd.value)
+            dst.append(nd.host)
+        self.inc_lock_ref(nid)
+        self.tickets[t] = ("write", nid)
+        cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int32)
+        return cat(src), cat(dst), t
+
+    def load_back(self, nid):
+        """Device slots for the nodes on nid's root path that are on the host only: returns
+        (host slots, device slots, ticket); the path stays locked until commit."""
+        path = self.path(nid)
+        todo = [nd for nd in path if not len(nd.value)]
+        self.inc_lock_ref(nid)
+        try:
+            got = self.alloc(sum(len(nd.key) for nd in todo))
+        except NoSpace:
+            self.dec_lock_ref(nid)
+            raise
+        t = self.next_ticket
+        self.next_ticket += 1
+        src, dst, o = [], [], 0
+        for nd in todo:
+            nd.value = got[o:o + len(nd.key)]
+            nd.pend = t
+            o += len(nd.key)
+            self.protected += len(nd.key)          # the path is locked
+            src.append(nd.host)
+            dst.append(nd.value)
+        self.tickets[t] = ("load", nid)
+        cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int32)
+        return cat(src), cat(dst), t
+
+    def commit(self, ticket, success=True):
+        """Resolve a copy.  A write-through that failed gives its host slots back; either way
+        the path is unlocked.  Only the write-through's commit carries an outcome on the page: a
+        load back is committed once its copy has run, and a failed one is refused."""
+        kind, nid = self.tickets[ticket]
+        if kind == "load" and not success:
+            raise ValueError("a load back is committed after its copy has run")
+        del self.tickets[ticket]
+        for nd in list(self.nodes.values()):
+            if nd is self.root or nd.pend != ticket:
+                continue
+            nd.pend = 0
+            if not success:
+                self.host_free[nd.host] = True
+                nd.host = np.zeros(0, np.int32)
+        self.dec_lock_ref(nid)
 
     # ---------------------------------------------------------------- views
     def path(self, nid):
@@ -270,7 +436,8 @@ class RadixTree:
         return out[::-1]
 
     def tree_tokens(self) -> int:
-        return sum(len(nd.key) for nd in self.nodes.values())
+        """Tokens on the device."""
+        return sum(len(nd.value) for nd in self.nodes.values())
 
     def stats(self) -> dict:
         return {
@@ -281,6 +448,8 @@ class RadixTree:
             "free": self.num_free(),
             "evicted_total": self.evicted_total,
             "clock": self.clock,
+            "host_tokens": sum(len(nd.host) for nd in self.nodes.values()),
+            "host_free": int(self.host_free.sum()),
         }
 
     def dump(self) -> str:
@@ -293,9 +462,12 @@ class RadixTree:
         def walk(nd, depth):
             for ft in sorted(nd.children):            # first tokens, or first pages as tuples
                 c = nd.children[ft]
-                lines.append("%d %d %d %d %d | %s | %s" % (
+                line = "%d %d %d %d %d | %s | %s" % (
                     depth, c.id, c.lock_ref, c.last_access, len(c.key),
-                    " ".join(map(str, c.key.tolist())), " ".join(map(str, c.value.tolist()))))
+                    " ".join(map(str, c.key.tolist())), " ".join(map(str, c.value.tolist())))
+                if self.host_slots:
+                    line += " | %s | %d" % (" ".join(map(str, c.host.tolist())), c.pend)
+                lines.append(line)
                 walk(c, depth + 1)
 
         walk(self.root, 0)

@@ -7,6 +7,7 @@ package only marshals torch tensors and numpy arrays into those calls.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -15,7 +16,7 @@ from ._lib import (Tree, Plan, RsError, NoSpaceError, StaleError, DTYPE_F32, DTY
 
 __all__ = ["Tree", "Plan", "RsError", "NoSpaceError", "StaleError", "store_kv", "extend_attention",
            "decode_attention", "merge_states", "DecodeWorkspace", "draft_tree_build", "tree_verify_attention",
-           "move_kv", "LIB_PATH"]
+           "move_kv", "copy_kv", "host_pool", "LIB_PATH"]
 
 _DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
@@ -88,6 +89,41 @@ def move_kv(k_pool, v_pool, src_slots, dst_slots, stream=None):
     _lib.move_kv(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
                  _dev(src_slots, "src_slots", torch.int32), _dev(dst_slots, "dst_slots", torch.int32),
                  src_slots.numel(), Hkv, D, _dtype(k_pool), _stream(stream))
+
+
+def host_pool(shape, dtype=torch.bfloat16):
+    """A host-tier pool: a CPU tensor in pinned memory from rs_host_alloc, which rs_copy_kv
+    may read and write (other host memory it refuses)."""
+    n = 1
+    for x in shape:
+        n *= int(x)
+    nbytes = max(n * torch.empty((), dtype=dtype).element_size(), 1)
+    arr = np.frombuffer(_lib.host_alloc(nbytes), dtype=np.uint8)
+    return torch.from_numpy(arr).view(dtype).view(*shape)
+
+
+def _pool(t: torch.Tensor, name: str, dtype=None):
+    """A device tensor, or a host pool (host_pool)."""
+    if not t.is_contiguous():
+        raise RsError(_lib.RS_E_INVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise RsError(_lib.RS_E_INVAL, f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def copy_kv(dst_k, dst_v, src_k, src_v, dst_slots, src_slots, stream=None):
+    """dst pools[dst_slots[r]] = src pools[src_slots[r]] (slot arrays device int32 [n]); pools
+    [rows, Hkv, D], on the device or pinned on the host (the host tier's copies)."""
+    R, Hkv, D = dst_k.shape
+    S = src_k.shape[0]
+    if tuple(src_k.shape[1:]) != (Hkv, D) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise RsError(_lib.RS_E_INVAL, "copy_kv: pool shapes differ")
+    if dst_slots.numel() != src_slots.numel():
+        raise RsError(_lib.RS_E_INVAL, "copy_kv: slot arrays differ in length")
+    _lib.copy_kv(_pool(dst_k, "dst_k"), _pool(dst_v, "dst_v", dst_k.dtype), _pool(src_k, "src_k", dst_k.dtype),
+                 _pool(src_v, "src_v", dst_k.dtype), _dev(dst_slots, "dst_slots", torch.int32),
+                 _dev(src_slots, "src_slots", torch.int32), src_slots.numel(), R, S, Hkv, D, _dtype(dst_k),
+                 _stream(stream))
 
 
 class DecodeWorkspace:

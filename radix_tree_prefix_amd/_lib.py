@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 
@@ -52,7 +53,8 @@ def _check(rc):
 class Stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "pool_slots", "nodes", "tree_tokens", "evictable", "protected", "free_slots", "evicted_total",
-        "clock", "matched_total", "match_calls", "insert_calls")] + [("reserved", C.c_int64 * 5)]
+        "clock", "matched_total", "match_calls", "insert_calls", "host_slots", "host_tokens", "host_free")] + \
+        [("reserved", C.c_int64 * 2)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
@@ -103,6 +105,16 @@ _SIGS = {
     "rs_tree_verify_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, _P, C.c_int32, C.c_int32, C.c_int32,
                                            C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P]),
     "rs_move_kv": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, C.c_int32, _P]),
+    "rs_copy_kv": (C.c_int, [_P, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                             C.c_int32, _P]),
+    "rs_host_alloc": (C.c_int, [C.c_int64, C.POINTER(C.c_void_p)]),
+    "rs_host_free": (C.c_int, [_P]),
+    "rs_host_tier_enable": (C.c_int, [_P, C.c_int64]),
+    "rs_match_prefix2": (C.c_int, [_P, _P, C.c_int64, _P, _P, _I64P, _I64P, _I64P, _I64P]),
+    "rs_write_through": (C.c_int, [_P, C.c_int64, C.c_int64, _P, _P, _I64P, _I64P]),
+    "rs_load_back": (C.c_int, [_P, C.c_int64, C.c_int64, _P, _P, _I64P, _I64P]),
+    "rs_commit": (C.c_int, [_P, C.c_int64, C.c_int32]),
+    "rs_evict_host": (C.c_int64, [_P, C.c_int64]),
     "rs_decode_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_float, C.c_int32, _P, _P, _P, C.c_int64, _P, _P, _P]),
     "rs_merge_states": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P]),
@@ -143,6 +155,7 @@ class Tree:
             raise RsError(RS_E_INVAL, lib.rs_last_error().decode())
         self._h = C.c_void_p(h)
         self.pool_slots = int(pool_slots)
+        self.host_slots = 0
 
     def close(self):
         if self._h:
@@ -214,6 +227,44 @@ class Tree:
         _check(lib.rs_schedule(self._h, tp, op, n, SCHED_POLICIES[policy], order.ctypes.data_as(C.c_void_p),
                                matched.ctypes.data_as(C.c_void_p)))
         return order, matched
+
+    # -------------------------------------------------------------- host tier
+    def enable_host(self, host_slots):
+        _check(lib.rs_host_tier_enable(self._h, int(host_slots)))
+        self.host_slots = int(host_slots)
+
+    def match2(self, tokens):
+        """(device slots, host slots, device length, total length, device node, last node)."""
+        tok, tp = _i32(tokens)
+        dev = np.empty(len(tok), np.int32)
+        host = np.empty(len(tok), np.int32)
+        dl, tl, dn, nd = C.c_int64(), C.c_int64(), C.c_int64(), C.c_int64()
+        _check(lib.rs_match_prefix2(self._h, tp, len(tok), dev.ctypes.data_as(C.c_void_p),
+                                    host.ctypes.data_as(C.c_void_p), C.byref(dl), C.byref(tl), C.byref(dn),
+                                    C.byref(nd)))
+        return dev[:dl.value], host[:tl.value - dl.value], dl.value, tl.value, dn.value, nd.value
+
+    def _pairs(self, fn, node, cap):
+        a = np.empty(cap, np.int32)
+        b = np.empty(cap, np.int32)
+        n, tk = C.c_int64(), C.c_int64()
+        _check(fn(self._h, int(node), cap, a.ctypes.data_as(C.c_void_p), b.ctypes.data_as(C.c_void_p),
+                  C.byref(n), C.byref(tk)))
+        return a[:n.value], b[:n.value], tk.value
+
+    def write_through(self, node):
+        """(device slots, host slots, ticket): the rows to copy to the host tier."""
+        return self._pairs(lib.rs_write_through, node, self.host_slots)
+
+    def load_back(self, node):
+        """(host slots, device slots, ticket): the rows to copy back to the device."""
+        return self._pairs(lib.rs_load_back, node, self.pool_slots)
+
+    def commit(self, ticket, success=True):
+        _check(lib.rs_commit(self._h, int(ticket), 1 if success else 0))
+
+    def evict_host(self, num_tokens):
+        return _check(lib.rs_evict_host(self._h, int(num_tokens)))
 
     def stats(self):
         s = Stats()
@@ -314,6 +365,21 @@ def tree_verify_attention(q, k_pool, v_pool, req_to_token, ld, prefix_lens, tree
     _check(lib.rs_tree_verify_attention(q, k_pool, v_pool, req_to_token, int(ld), prefix_lens, tree_mask, int(B),
                                         int(n), int(Hq), int(Hkv), int(D), float(sm_scale), int(dtype), out,
                                         C.c_void_p(stream)))
+
+
+def host_alloc(nbytes):
+    """A pinned host block from rs_host_alloc as a ctypes byte array; rs_host_free runs when the
+    array (and every view of it) is gone."""
+    p = C.c_void_p()
+    _check(lib.rs_host_alloc(int(nbytes), C.byref(p)))
+    buf = (C.c_uint8 * int(nbytes)).from_address(p.value)
+    weakref.finalize(buf, lib.rs_host_free, C.c_void_p(p.value))
+    return buf
+
+
+def copy_kv(dst_k, dst_v, src_k, src_v, dst_slots, src_slots, n, dst_rows, src_rows, Hkv, D, dtype, stream=0):
+    _check(lib.rs_copy_kv(dst_k, dst_v, src_k, src_v, dst_slots, src_slots, int(n), int(dst_rows), int(src_rows),
+                          int(Hkv), int(D), int(dtype), C.c_void_p(stream)))
 
 
 def move_kv(k_pool, v_pool, src, dst, n, Hkv, D, dtype, stream=0):

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "librs.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["tree.cpp", "schedule.cpp", "draft.cpp", "plan.cpp", "kernels.hip"]
+SOURCES = ["tree.cpp", "schedule.cpp", "draft.cpp", "plan.cpp", "kernels.hip", "hostpool.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # no packed-fp32 instructions in device code

@@ -2,9 +2,11 @@
 #pragma once
 
 #include <cstdint>
+#include <map>
 #include <memory>
 #include <string>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "rs.h"
@@ -24,7 +26,9 @@ int64_t diverge(const int32_t* a, const int32_t* b, int64_t n);
 struct Node {
   int64_t id = 0;
   std::vector<int32_t> key;     // token run on the edge into this node
-  std::vector<int32_t> value;   // one pool slot per key token
+  std::vector<int32_t> value;   // one pool slot per key token; empty: the node is on the host only
+  std::vector<int32_t> host;    // host-tier slots; empty: no host copy
+  int64_t pend = 0;             // ticket of a copy in flight (0: none)
   Node* parent = nullptr;
   // keyed on the child's first token; with pages > 1 token, siblings may share it and
   // differ later in their first page (the page is the key)
@@ -65,6 +69,9 @@ struct rs_tree {
   rs::Node root;
   std::unordered_map<int64_t, std::unique_ptr<rs::Node>> nodes;   // id -> node (root excluded)
   rs::SlotAllocator alloc;
+  std::unique_ptr<rs::SlotAllocator> host;          // host tier (null until enabled)
+  std::map<int64_t, std::pair<int, int64_t>> tickets;  // ticket -> (0 write / 1 load, locked node)
+  int64_t next_ticket = 1;
   int64_t next_id = 1;
   uint64_t clock = 0;
   int64_t evictable = 0, protected_ = 0, evicted_total = 0, tree_tokens = 0;
@@ -84,6 +91,11 @@ struct rs_tree {
   void lock(rs::Node* nd);
   int unlock(rs::Node* nd);
   int64_t evict(int64_t need);
+  int64_t evict_host(int64_t need);
+  void drop_host_subtree(rs::Node* x);            // frees and unlinks x's (host-only) descendants
+  int alloc_host(int64_t n, int32_t* out);
+  bool device_leaf(const rs::Node* n) const;
+  std::vector<rs::Node*> path(rs::Node* nd);        // root's child .. nd
   int alloc_slots(int64_t n, int32_t* out);
   int64_t depth_tokens(const rs::Node* nd) const;
 };

@@ -167,15 +167,22 @@ Node* rs_tree::split(Node* child, int64_t k) {
   Node* u = up.get();
   u->id = next_id++;
   u->key.assign(child->key.begin(), child->key.begin() + k);
-  u->value.assign(child->value.begin(), child->value.begin() + k);
+  if (!child->value.empty()) {            // empty: on the host only
+    u->value.assign(child->value.begin(), child->value.begin() + k);
+    child->value.erase(child->value.begin(), child->value.begin() + k);
+  }
   u->parent = child->parent;
   u->lock_ref = child->lock_ref;
   u->last_access = child->last_access;
   u->priority = child->priority;
+  u->pend = child->pend;
+  if (!child->host.empty()) {
+    u->host.assign(child->host.begin(), child->host.begin() + k);
+    child->host.erase(child->host.begin(), child->host.begin() + k);
+  }
   unlink(u->parent, child);
   link(u->parent, u);
   child->key.erase(child->key.begin(), child->key.begin() + k);
-  child->value.erase(child->value.begin(), child->value.begin() + k);
   child->parent = u;
   link(u, child);
   nodes.emplace(u->id, std::move(up));
@@ -189,7 +196,7 @@ int64_t rs_tree::match(const int32_t* tok, int64_t n, int32_t* out, Node** end) 
   int64_t pos = 0;
   while (pos + ps <= n) {                 // whole pages only
     Node* c = child_at(node, tok + pos);
-    if (!c) break;
+    if (!c || c->value.empty()) break;   // absent, or on the host only: not a device match
     c->last_access = clock;
     int64_t len = int64_t(c->key.size());
     int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos)) / ps * ps;
@@ -227,6 +234,12 @@ int rs_tree::insert(const int32_t* tok, int32_t* slots, int64_t n, int64_t* pref
     int64_t len = int64_t(c->key.size());
     int64_t k = rs::diverge(c->key.data(), tok + pos, std::min(len, n - pos)) / ps * ps;
     if (k < len) c = split(c, k);
+    if (c->value.empty()) {               // on the host only: it takes the caller's device slots
+      c->value.assign(slots + pos, slots + pos + k);
+      if (c->lock_ref > 0) protected_ += k;
+      else evictable += k;
+      tree_tokens += k;
+    }
     differ.clear();
     for (int64_t i = 0; i < k; ++i)
       if (slots[pos + i] != c->value[i]) differ.push_back(slots[pos + i]);
@@ -258,8 +271,8 @@ int rs_tree::insert(const int32_t* tok, int32_t* slots, int64_t n, int64_t* pref
 void rs_tree::lock(Node* nd) {
   for (; nd != &root; nd = nd->parent) {
     if (nd->lock_ref == 0) {
-      evictable -= int64_t(nd->key.size());
-      protected_ += int64_t(nd->key.size());
+      evictable -= int64_t(nd->value.size());
+      protected_ += int64_t(nd->value.size());
     }
     ++nd->lock_ref;
   }
@@ -270,12 +283,19 @@ int rs_tree::unlock(Node* nd) {
     return rs::fail(RS_E_INVAL, "rs_dec_lock_ref: node " + std::to_string(nd->id) + " is not locked");
   for (; nd != &root; nd = nd->parent) {
     if (nd->lock_ref == 1) {
-      evictable += int64_t(nd->key.size());
-      protected_ -= int64_t(nd->key.size());
+      evictable += int64_t(nd->value.size());
+      protected_ -= int64_t(nd->value.size());
     }
     --nd->lock_ref;
   }
   return RS_OK;
+}
+
+bool rs_tree::device_leaf(const Node* n) const {
+  if (n->value.empty() || n->lock_ref != 0) return false;
+  for (auto& kv : n->children)
+    if (!kv.second->value.empty()) return false;
+  return true;
 }
 
 int64_t rs_tree::evict(int64_t need) {
@@ -283,26 +303,82 @@ int64_t rs_tree::evict(int64_t need) {
   std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
   for (auto& kv : nodes) {
     Node* n = kv.second.get();
-    if (n->children.empty() && n->lock_ref == 0) heap.emplace(n->priority, n->last_access, n->id);
+    if (device_leaf(n)) heap.emplace(n->priority, n->last_access, n->id);
   }
   int64_t freed = 0;
   while (freed < need && !heap.empty()) {
     int64_t id = std::get<2>(heap.top());
     heap.pop();
     Node* x = nodes[id].get();
-    int64_t len = int64_t(x->key.size());
+    int64_t len = int64_t(x->value.size());
     alloc.give_back(x->value.data(), len);
     freed += len;
     evictable -= len;
     tree_tokens -= len;
     Node* p = x->parent;
-    unlink(p, x);
-    nodes.erase(id);
-    if (p != &root && p->children.empty() && p->lock_ref == 0)
-      heap.emplace(p->priority, p->last_access, p->id);
+    if (!x->host.empty() && x->pend == 0) {
+      x->value.clear();                   // a finished host copy: the node stays, on the host
+    } else {
+      drop_host_subtree(x);               // children left are on the host only; they go too
+      unlink(p, x);
+      nodes.erase(id);
+    }
+    if (p != &root && device_leaf(p)) heap.emplace(p->priority, p->last_access, p->id);
   }
   evicted_total += freed;
   return freed;
+}
+
+void rs_tree::drop_host_subtree(Node* x) {
+  std::vector<Node*> kids;
+  for (auto& kv : x->children) kids.push_back(kv.second);
+  for (Node* c : kids) {
+    drop_host_subtree(c);
+    if (host) host->give_back(c->host.data(), int64_t(c->host.size()));
+    unlink(x, c);
+    nodes.erase(c->id);
+  }
+}
+
+int64_t rs_tree::evict_host(int64_t need) {
+  typedef std::tuple<int64_t, uint64_t, int64_t> Key;
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+  auto host_leaf = [&](const Node* n) {
+    return n->value.empty() && n->children.empty() && n->lock_ref == 0 && n->pend == 0;
+  };
+  for (auto& kv : nodes)
+    if (host_leaf(kv.second.get())) heap.emplace(kv.second->priority, kv.second->last_access, kv.second->id);
+  int64_t freed = 0;
+  while (freed < need && !heap.empty()) {
+    int64_t id = std::get<2>(heap.top());
+    heap.pop();
+    Node* x = nodes[id].get();
+    host->give_back(x->host.data(), int64_t(x->host.size()));
+    freed += int64_t(x->host.size());
+    Node* p = x->parent;
+    unlink(p, x);
+    nodes.erase(id);
+    if (p != &root && host_leaf(p)) heap.emplace(p->priority, p->last_access, p->id);
+  }
+  return freed;
+}
+
+int rs_tree::alloc_host(int64_t n, int32_t* out) {
+  if (host->num_free() < n) {
+    evict_host(n - host->num_free());
+    if (host->num_free() < n)
+      return rs::fail(RS_E_NOSPACE, "host tier: " + std::to_string(n) + " slots wanted, " +
+                                        std::to_string(host->num_free()) + " free after evicting every host leaf");
+  }
+  host->take(n, out);
+  return RS_OK;
+}
+
+std::vector<Node*> rs_tree::path(Node* nd) {
+  std::vector<Node*> p;
+  for (; nd != &root; nd = nd->parent) p.push_back(nd);
+  std::reverse(p.begin(), p.end());
+  return p;
 }
 
 int rs_tree::alloc_slots(int64_t n, int32_t* out) {
@@ -473,6 +549,167 @@ int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new, i
   RS_GUARD_END
 }
 
+int rs_host_tier_enable(rs_tree* t, int64_t host_slots) {
+  if (!t || host_slots <= 0 || host_slots > (int64_t(1) << 31) - 1)
+    return rs::fail(RS_E_INVAL, "rs_host_tier_enable: bad arguments");
+  if (t->ps != 1) return rs::fail(RS_E_UNSUPPORTED, "rs_host_tier_enable: page size 1 only");
+  if (t->host) return rs::fail(RS_E_INVAL, "rs_host_tier_enable: the host tier is already on");
+  RS_GUARD_BEGIN
+  t->host = std::make_unique<rs::SlotAllocator>(host_slots, 1);
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_match_prefix2(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_dev_slots, int32_t* out_host_slots,
+                     int64_t* out_dev_len, int64_t* out_len, int64_t* out_dev_node, int64_t* out_node) {
+  if (!t || n < 0 || (n && (!tokens || !out_dev_slots || !out_host_slots)) || !out_dev_len || !out_len ||
+      !out_dev_node || !out_node)
+    return rs::fail(RS_E_INVAL, "rs_match_prefix2: bad arguments");
+  RS_GUARD_BEGIN
+  ++t->clock;
+  ++t->match_calls;
+  Node* node = &t->root;
+  Node* dev_node = &t->root;
+  int64_t pos = 0, dev_len = 0;
+  while (pos < n) {
+    Node* c = t->child_at(node, tokens + pos);
+    if (!c) break;
+    c->last_access = t->clock;
+    const int64_t len = int64_t(c->key.size());
+    const int64_t k = rs::diverge(c->key.data(), tokens + pos, std::min(len, n - pos));
+    if (k < len) c = t->split(c, k);
+    if (!c->value.empty() && dev_len == pos) {
+      std::memcpy(out_dev_slots + pos, c->value.data(), size_t(k) * 4);
+      dev_node = c;
+      dev_len = pos + k;
+    } else {
+      std::memcpy(out_host_slots + (pos - dev_len), c->host.data(), size_t(k) * 4);
+    }
+    pos += k;
+    node = c;
+  }
+  t->matched_total += dev_len;
+  *out_dev_len = dev_len;
+  *out_len = pos;
+  *out_dev_node = dev_node->id;
+  *out_node = node->id;
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_write_through(rs_tree* t, int64_t node, int64_t cap, int32_t* out_dev_slots, int32_t* out_host_slots,
+                     int64_t* out_n, int64_t* out_ticket) {
+  if (!t || cap < 0 || (cap && (!out_dev_slots || !out_host_slots)) || !out_n || !out_ticket)
+    return rs::fail(RS_E_INVAL, "rs_write_through: bad arguments");
+  if (!t->host) return rs::fail(RS_E_INVAL, "rs_write_through: the host tier is off");
+  Node* nd = t->find(node);
+  if (!nd) return rs::fail(RS_E_STALE, "rs_write_through: node " + std::to_string(node) + " is gone");
+  RS_GUARD_BEGIN
+  std::vector<Node*> todo;
+  int64_t need = 0;
+  for (Node* x : t->path(nd)) {
+    if (x->value.empty()) return rs::fail(RS_E_INVAL, "rs_write_through: the path is not on the device");
+    if (x->host.empty() && x->pend == 0) {
+      todo.push_back(x);
+      need += int64_t(x->key.size());
+    }
+  }
+  if (need > cap) return rs::fail(RS_E_INVAL, "rs_write_through: " + std::to_string(need) + " pairs, capacity " +
+                                                  std::to_string(cap));
+  std::vector<int32_t> got(size_t(need) + 1);
+  int rc = t->alloc_host(need, got.data());
+  if (rc != RS_OK) return rc;
+  const int64_t tk = t->next_ticket++;
+  int64_t o = 0;
+  for (Node* x : todo) {
+    const int64_t len = int64_t(x->key.size());
+    x->host.assign(got.begin() + o, got.begin() + o + len);
+    x->pend = tk;
+    std::memcpy(out_dev_slots + o, x->value.data(), size_t(len) * 4);
+    std::memcpy(out_host_slots + o, x->host.data(), size_t(len) * 4);
+    o += len;
+  }
+  t->lock(nd);
+  t->tickets[tk] = {0, node};
+  *out_n = need;
+  *out_ticket = tk;
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_load_back(rs_tree* t, int64_t node, int64_t cap, int32_t* out_host_slots, int32_t* out_dev_slots,
+                 int64_t* out_n, int64_t* out_ticket) {
+  if (!t || cap < 0 || (cap && (!out_dev_slots || !out_host_slots)) || !out_n || !out_ticket)
+    return rs::fail(RS_E_INVAL, "rs_load_back: bad arguments");
+  if (!t->host) return rs::fail(RS_E_INVAL, "rs_load_back: the host tier is off");
+  Node* nd = t->find(node);
+  if (!nd) return rs::fail(RS_E_STALE, "rs_load_back: node " + std::to_string(node) + " is gone");
+  RS_GUARD_BEGIN
+  std::vector<Node*> todo;
+  int64_t need = 0;
+  for (Node* x : t->path(nd))
+    if (x->value.empty()) {
+      todo.push_back(x);
+      need += int64_t(x->key.size());
+    }
+  if (need > cap) return rs::fail(RS_E_INVAL, "rs_load_back: " + std::to_string(need) + " pairs, capacity " +
+                                                  std::to_string(cap));
+  t->lock(nd);
+  std::vector<int32_t> got(size_t(need) + 1);
+  int rc = t->alloc_slots(need, got.data());
+  if (rc != RS_OK) {
+    t->unlock(nd);
+    return rc;
+  }
+  const int64_t tk = t->next_ticket++;
+  int64_t o = 0;
+  for (Node* x : todo) {
+    const int64_t len = int64_t(x->key.size());
+    x->value.assign(got.begin() + o, got.begin() + o + len);
+    x->pend = tk;
+    t->protected_ += len;                 // the path is locked
+    t->tree_tokens += len;
+    std::memcpy(out_host_slots + o, x->host.data(), size_t(len) * 4);
+    std::memcpy(out_dev_slots + o, x->value.data(), size_t(len) * 4);
+    o += len;
+  }
+  t->tickets[tk] = {1, node};
+  *out_n = need;
+  *out_ticket = tk;
+  return RS_OK;
+  RS_GUARD_END
+}
+
+int rs_commit(rs_tree* t, int64_t ticket, int32_t success) {
+  if (!t) return rs::fail(RS_E_INVAL, "rs_commit: null tree");
+  auto it = t->tickets.find(ticket);
+  if (it == t->tickets.end()) return rs::fail(RS_E_INVAL, "rs_commit: unknown ticket " + std::to_string(ticket));
+  if (it->second.first == 1 && !success)
+    return rs::fail(RS_E_INVAL, "rs_commit: a load back is committed after its copy has run");
+  RS_GUARD_BEGIN
+  const int64_t node = it->second.second;
+  t->tickets.erase(it);
+  for (auto& kv : t->nodes) {
+    Node* x = kv.second.get();
+    if (x->pend != ticket) continue;
+    x->pend = 0;
+    if (!success) {                       // a write-through that failed: no host copy
+      t->host->give_back(x->host.data(), int64_t(x->host.size()));
+      x->host.clear();
+    }
+  }
+  return t->unlock(t->find(node));
+  RS_GUARD_END
+}
+
+int64_t rs_evict_host(rs_tree* t, int64_t num_tokens) {
+  if (!t || num_tokens < 0) return rs::fail(RS_E_INVAL, "rs_evict_host: bad arguments");
+  if (!t->host) return rs::fail(RS_E_INVAL, "rs_evict_host: the host tier is off");
+  RS_GUARD_BEGIN
+  return t->evict_host(num_tokens);
+  RS_GUARD_END
+}
+
 int rs_stats(const rs_tree* t, rs_stats_t* out) {
   if (!t || !out) return rs::fail(RS_E_INVAL, "rs_stats: bad arguments");
   std::memset(out, 0, sizeof(*out));
@@ -487,6 +724,11 @@ int rs_stats(const rs_tree* t, rs_stats_t* out) {
   out->matched_total = t->matched_total;
   out->match_calls = t->match_calls;
   out->insert_calls = t->insert_calls;
+  if (t->host) {
+    out->host_slots = t->host->capacity();
+    out->host_free = t->host->num_free();
+    for (auto& kv : t->nodes) out->host_tokens += int64_t(kv.second->host.size());
+  }
   return RS_OK;
 }
 
@@ -507,17 +749,27 @@ int rs_tree_dump(const rs_tree* t, char* buf, int64_t cap, int64_t* need) {
     });
     for (auto it = kids.rbegin(); it != kids.rend(); ++it) st.emplace_back(*it, depth);
   };
+  auto field = [&](const std::vector<int32_t>& v) {     // " | " then the numbers, space-separated
+    s += " | ";
+    for (size_t i = 0; i < v.size(); ++i) {
+      if (i) s += ' ';
+      s += std::to_string(v[i]);
+    }
+  };
   push_children(&t->root, 0);
   while (!st.empty()) {
     const Node* c = st.back().first;
     int depth = st.back().second;
     st.pop_back();
-    std::snprintf(tmp, sizeof tmp, "%d %lld %d %llu %zu |", depth, (long long)c->id, c->lock_ref,
+    std::snprintf(tmp, sizeof tmp, "%d %lld %d %llu %zu", depth, (long long)c->id, c->lock_ref,
                   (unsigned long long)c->last_access, c->key.size());
     s += tmp;
-    for (int32_t x : c->key) { s += ' '; s += std::to_string(x); }
-    s += " |";
-    for (int32_t x : c->value) { s += ' '; s += std::to_string(x); }
+    field(c->key);
+    field(c->value);
+    if (t->host) {
+      field(c->host);
+      s += " | " + std::to_string(c->pend);
+    }
     s += '\n';
     push_children(c, depth + 1);
   }

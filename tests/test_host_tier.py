@@ -1,0 +1,323 @@
+"""Two-tier cache (device slots + a host tier): the library against the oracle on random
+operation sequences (dumps, stats and every returned slot bit-exact), the oracle against
+brute force and data invariants, and the rules of "SGLang: the tree, ..."
+(ai.thesatyajit.com), "What the C++ tree is actually for", on hand-built cases: a match
+reports the device part and the host part with a node per tier, leaf-ness on the device
+counts device-resident children only, writes to the host and loads back are transactions
+that a later commit resolves."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import radix_tree_prefix_amd as rs
+
+
+def _both(pool, host):
+    o, c = oracle.RadixTree(pool), rs.Tree(pool)
+    o.enable_host(host)
+    c.enable_host(host)
+    return o, c
+
+
+def _admit(t, seq):
+    """Admit seq with nothing new, then unlock: the tree holds seq afterwards."""
+    if isinstance(t, oracle.RadixTree):
+        row, node, m = oracle.admit(t, seq, len(seq), 0)
+    else:
+        row, node, m = t.admit(seq, len(seq), 0)
+    t.dec_lock_ref(node)
+    return row, node, m
+
+
+def test_rules_by_hand():
+    for t in _both(8, 8):
+        a = np.array([1, 2, 3, 4, 5], np.int32)
+        _row, node, _m = _admit(t, a)
+        dev, host, tk = t.write_through(node)
+        assert list(dev) == [0, 1, 2, 3, 4] and list(host) == [0, 1, 2, 3, 4]
+        assert t.evict(5) == 0                     # in flight: the path is locked until commit
+        t.commit(tk, True)
+        assert t.evict(3) == 5                     # the whole leaf leaves the device ...
+        got, _n = t.match_prefix(a)
+        assert len(got) == 0                       # ... a device match stops before it ...
+        d, h, dl, tl, dn, ln = t.match2(a)
+        assert (dl, tl, dn, ln) == (0, 5, 0, node) and list(h) == [0, 1, 2, 3, 4]   # ... it is on the host
+        src, dst, tk = t.load_back(node)
+        assert list(src) == [0, 1, 2, 3, 4] and list(dst) == [0, 1, 2, 3, 4]
+        t.commit(tk, True)
+        d, h, dl, tl, dn, ln = t.match2(a)
+        assert (dl, tl, dn) == (5, 5, node) and len(h) == 0
+        assert t.evict(1) == 5                     # back on the host only
+        assert t.evict_host(1) == 5                # and out of the tree
+        assert t.match2(a)[3] == 0
+
+
+def test_failed_commits_release():
+    for t in _both(8, 8):
+        a = np.array([7, 7, 7], np.int32)
+        _row, node, _m = _admit(t, a)
+        _d, _h, tk = t.write_through(node)
+        t.commit(tk, False)                        # the copy failed: no host copy
+        assert t.evict(1) == 3 and t.match2(a)[3] == 0
+        _row, node, _m = _admit(t, a)
+        _d, _h, tk = t.write_through(node)
+        t.commit(tk, True)
+        t.evict(3)
+        _s, _dst, tk = t.load_back(node)
+        with pytest.raises((ValueError, rs.RsError)):
+            t.commit(tk, False)                    # a load back has no failed outcome
+        t.commit(tk, True)
+        _d, _h, dl, tl, _dn, _ln = t.match2(a)
+        assert (dl, tl) == (3, 3)
+
+
+def test_insert_over_host_only_takes_the_callers_slots():
+    o, c = _both(8, 8)
+    for t in (o, c):
+        _row, node, _m = _admit(t, np.array([1, 2, 3], np.int32))
+        _d, _h, tk = t.write_through(node)
+        t.commit(tk, True)
+        t.evict(3)
+        row, node2, m = _admit(t, np.array([1, 2, 3, 4], np.int32))   # re-prefill over the host copy
+        assert m == 0 and list(row) == [0, 1, 2, 3]
+    assert c.dump() == o.dump()
+    assert "| 0 1 2 | 0 1 2 | 0" in c.dump()           # device slots back, host copy kept
+
+
+def test_device_eviction_of_a_parent_without_host_copy_drops_its_host_subtree():
+    """A failed write-through of an upper node after a finished one below leaves a host copy
+    under a node without one; when that node leaves the device it leaves the tree, and its
+    host-only subtree with it."""
+    o, c = _both(16, 16)
+    for t in (o, c):
+        _r, n1, _m = _admit(t, np.array([1, 1], np.int32))
+        _r, n2, _m = _admit(t, np.array([1, 1, 2, 2], np.int32))
+        _d, _h, tk1 = t.write_through(n1)
+        _d, _h, tk2 = t.write_through(n2)          # the upper node is in flight: only the lower one
+        t.commit(tk2, True)
+        t.commit(tk1, False)
+        assert t.evict(16) == 4
+    assert c.dump() == o.dump() == ""
+    assert c.stats()["host_free"] == o.stats()["host_free"] == 16
+
+
+def _h(tokens):
+    """Stand-in for the KV row of the last token of this prefix."""
+    x = 1469598103934665603
+    for v in tokens:
+        x = ((x ^ (int(v) + 1)) * 1099511628211) % (1 << 61)
+    return x
+
+
+class Pools:
+    """Device and host K/V stand-ins: one int per slot."""
+
+    def __init__(self, pool, host):
+        self.dev = np.full(pool, -1, np.int64)
+        self.host = np.full(host, -1, np.int64)
+
+
+def _check_invariants(t: oracle.RadixTree, pools: Pools, tickets):
+    kinds = {tk: kind for tk, (kind, _nid) in tickets.items()}
+    assert t.num_free() + t.tree_tokens() == t.pool_slots
+    assert int(t.host_free.sum()) + sum(len(nd.host) for nd in t.nodes.values()) == t.host_slots
+
+    def walk(nd, prefix, on_dev):
+        for c in nd.children.values():
+            toks = prefix + [int(x) for x in c.key]
+            if not on_dev:
+                assert not len(c.value), "a device node under a host-only one"
+            if c.pend:
+                assert c.lock_ref > 0, "a copy in flight on an unlocked node"
+            for j in range(len(c.key)):
+                want = _h(toks[:len(prefix) + j + 1])
+                if len(c.value) and not (c.pend and kinds[c.pend] == "load"):
+                    assert pools.dev[c.value[j]] == want
+                if len(c.host) and not (c.pend and kinds[c.pend] == "write"):
+                    assert pools.host[c.host[j]] == want
+            walk(c, toks, bool(len(c.value)))
+
+    walk(t.root, [], True)
+
+
+OPS = ("admit", "match", "match2", "unlock", "evict", "evict_host", "write", "backup", "load", "load_any",
+       "commit")
+
+
+def _both_or_none(fn):
+    """fn(tree) on the oracle and the library: both raise NoSpace, or neither (results returned)."""
+    res = []
+    for t in _both_or_none.trees:
+        try:
+            res.append(fn(t))
+        except (oracle.NoSpace, rs.NoSpaceError):
+            res.append(None)
+    assert (res[0] is None) == (res[1] is None)
+    return res if res[0] is not None else None
+
+
+def _run_ops(ops, pool, host, seen=None):
+    """Apply ops to the oracle and the library; after every op the dumps, stats and every
+    returned slot agree, and the oracle's tree holds the invariants (slot conservation per
+    tier, host-only subtrees, locked copies in flight, the rows the slots hold)."""
+    ot, ct = _both(pool, host)
+    _both_or_none.trees = (ot, ct)
+    pools = Pools(pool, host)
+    locks, tickets = [], {}
+    seen = seen if seen is not None else {}
+
+    def note(key):
+        seen[key] = seen.get(key, 0) + 1
+
+    def host_only():
+        return sorted(n for n, nd in ot.nodes.items() if n and not len(nd.value))
+
+    def transfer(kind, fn, node):
+        r = _both_or_none(lambda t: fn(t, node))
+        if r:
+            (a1, b1, t1), (a2, b2, t2) = r
+            assert t1 == t2
+            np.testing.assert_array_equal(a1, a2)
+            np.testing.assert_array_equal(b1, b2)
+            tickets[t1] = (kind, (a1, b1))
+            note(kind + ("" if len(a1) else "_empty"))
+            return t1
+
+    def commit(tk, ok):
+        kind, (src, dst) = tickets.pop(tk)
+        if ok:                                          # the copy ran before the commit
+            if kind == "write":
+                pools.host[dst] = pools.dev[src]
+            else:
+                pools.dev[dst] = pools.host[src]
+        ot.commit(tk, ok)
+        ct.commit(tk, ok)
+        note("commit_ok" if ok else "commit_fail")
+
+    for op, seq, k in ops:
+        seq = np.array(seq, dtype=np.int32)
+        if op == "admit":
+            before = len(host_only())
+            r = _both_or_none(lambda t: _admit(t, seq))
+            if r:
+                (orow, onode, om), (crow, cnode, cm) = r
+                assert (onode, om) == (cnode, cm)
+                np.testing.assert_array_equal(orow, crow)
+                for j in range(om, len(seq)):           # the re-prefill writes the rows
+                    pools.dev[orow[j]] = _h(seq[:j + 1])
+                if len(host_only()) < before:
+                    note("adopt")
+        elif op == "match":
+            a, an = ot.match_prefix(seq)
+            b, bn = ct.match_prefix(seq)
+            assert an == bn
+            np.testing.assert_array_equal(a, b)
+            if an:
+                ot.inc_lock_ref(an)
+                ct.inc_lock_ref(bn)
+                locks.append(an)
+        elif op == "match2":
+            a, b = ot.match2(seq), ct.match2(seq)
+            assert a[2:] == b[2:]
+            np.testing.assert_array_equal(a[0], b[0])
+            np.testing.assert_array_equal(a[1], b[1])
+            if a[3] > a[2]:
+                note("match2_host")
+        elif op == "unlock" and locks:
+            n = locks.pop(k % len(locks))
+            ot.dec_lock_ref(n)
+            ct.dec_lock_ref(n)
+        elif op == "evict":
+            assert ot.evict(k) == ct.evict(k)
+        elif op == "evict_host":
+            got = ot.evict_host(k)
+            assert got == ct.evict_host(k)
+            if got:
+                note("evict_host")
+        elif op in ("write", "backup"):
+            _a, n = ot.match_prefix(seq)
+            _b, n2 = ct.match_prefix(seq)
+            assert n == n2
+            if n:
+                tk = transfer("write", lambda t, x: t.write_through(x), n)
+                if tk is not None and op == "backup":
+                    commit(tk, True)
+        elif op == "load":
+            ln = ot.match2(seq)[5]
+            assert ct.match2(seq)[5] == ln
+            if ln:
+                transfer("load", lambda t, x: t.load_back(x), ln)
+        elif op == "load_any":
+            h = host_only()
+            if h:
+                transfer("load", lambda t, x: t.load_back(x), h[k % len(h)])
+        elif op == "commit" and tickets:
+            tk = sorted(tickets)[k % len(tickets)]
+            commit(tk, bool(k & 1) or k == 0 or tickets[tk][0] == "load")
+        assert ct.dump() == ot.dump()
+        cs, os_ = ct.stats(), ot.stats()
+        assert (cs["evictable"], cs["protected"], cs["free_slots"], cs["tree_tokens"], cs["host_tokens"],
+                cs["host_free"]) == (os_["evictable"], os_["protected"], os_["free"], os_["tree_tokens"],
+                                     os_["host_tokens"], os_["host_free"])
+        _check_invariants(ot, pools, {tk: (v[0], None) for tk, v in tickets.items()})
+    return seen
+
+
+seq_st = st.lists(st.integers(0, 2), min_size=1, max_size=10)
+op_st = st.tuples(st.sampled_from(OPS), seq_st, st.integers(0, 15))
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(op_st, min_size=1, max_size=50), st.integers(4, 24), st.integers(4, 24))
+def test_random_ops_match_oracle(ops, pool, host):
+    _run_ops(ops, pool, host)
+
+
+def test_seeded_long_runs_reach_every_path():
+    """Longer seeded sequences; the run must pass through every host-tier path."""
+    rng = np.random.default_rng(11)
+    seen = {}
+    for _ in range(500):
+        ops = [(OPS[rng.integers(len(OPS))], list(rng.integers(0, 3, rng.integers(1, 11))), int(rng.integers(0, 16)))
+               for _ in range(rng.integers(20, 80))]
+        _run_ops(ops, int(rng.integers(6, 30)), int(rng.integers(6, 30)), seen)
+    for key in ("write", "load", "adopt", "match2_host", "evict_host", "commit_ok", "commit_fail"):
+        assert seen.get(key, 0) >= 10, (key, seen)
+
+
+def _path_tokens(t, nid):
+    return np.concatenate([n.key for n in t.path(nid)]) if nid else np.zeros(0, np.int32)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.tuples(st.lists(st.integers(0, 2), min_size=1, max_size=10), st.booleans()),
+                min_size=1, max_size=8), st.lists(st.integers(0, 2), min_size=0, max_size=12),
+       st.integers(0, 30))
+def test_oracle_match2_is_longest_prefix_per_tier(seqs, q, ev):
+    """Brute force: the total match is the longest prefix shared with any path in the tree;
+    the device part the longest shared with a path on the device."""
+    t = oracle.RadixTree(64)
+    t.enable_host(64)
+    for s, back in seqs:
+        s = np.array(s, np.int32)
+        _row, node, _m = _admit(t, s)
+        if back:
+            _d, _h2, tk = t.write_through(node)
+            t.commit(tk, True)
+    t.evict(ev)
+    q = np.array(q, np.int32)
+    want_all = max([oracle.common_prefix_len(_path_tokens(t, n), q) for n in t.nodes] + [0])
+    want_dev = max([oracle.common_prefix_len(_path_tokens(t, n), q) for n, nd in t.nodes.items()
+                    if n and len(nd.value)] + [0])
+    dev, host, dl, tl, _dn, _ln = t.match2(q)
+    assert (dl, tl) == (want_dev, want_all)
+    assert len(dev) == dl and len(host) == tl - dl
+    got, _n = t.match_prefix(q)
+    assert len(got) == dl
+
+
+def test_host_tier_rejects_pages():
+    t = rs.Tree(64, 4)
+    with pytest.raises(rs.RsError):
+        t.enable_host(64)
