@@ -24,7 +24,8 @@
  *  - Return value: RS_OK (0) or a negative RS_E_* code; calls returning a count
  *    return it (>= 0) or a negative code.  rs_last_error() gives a message for
  *    the calling thread's last failure.  Nothing throws across the ABI.
- *  - Ownership: the library owns only rs_tree and rs_plan objects.  Every array
+ *  - Ownership: the library owns only rs_tree and rs_plan objects (and hands out
+ *    pinned host blocks from rs_host_alloc, which the caller then owns).  Every array
  *    argument is owned by the caller and only read or written during the call,
  *    except device arrays of asynchronous calls (see below).
  *  - Host vs device: "host" arrays are ordinary CPU memory; "device" arrays are
@@ -358,7 +359,9 @@ int rs_move_kv(void* k_pool, void* v_pool, const int32_t* src_slots, const int32
 
 /* Pinned host memory for the host tier's K/V pools [T "What the C++ tree is actually for"],
  * mapped for the GPU at its host address (RS_E_UNSUPPORTED if the runtime maps it elsewhere,
- * RS_E_NOSPACE if it cannot be had).  The caller owns it until rs_host_free. */
+ * RS_E_NOSPACE if it cannot be had).  The caller owns it until rs_host_free, which must come
+ * after every copy that reads or writes it has completed (RS_E_INVAL for a pointer that is not
+ * the start of such a block). */
 int rs_host_alloc(int64_t bytes, void** out);
 int rs_host_free(void* p);
 

@@ -688,6 +688,8 @@ int rs_commit(rs_tree* t, int64_t ticket, int32_t success) {
     return rs::fail(RS_E_INVAL, "rs_commit: a load back is committed after its copy has run");
   RS_GUARD_BEGIN
   const int64_t node = it->second.second;
+  Node* nd = t->find(node);               // locked since the transaction began, so still there
+  if (!nd) return rs::fail(RS_E_STALE, "rs_commit: node " + std::to_string(node) + " is gone");
   t->tickets.erase(it);
   for (auto& kv : t->nodes) {
     Node* x = kv.second.get();
@@ -698,7 +700,7 @@ int rs_commit(rs_tree* t, int64_t ticket, int32_t success) {
       x->host.clear();
     }
   }
-  return t->unlock(t->find(node));
+  return t->unlock(nd);
   RS_GUARD_END
 }
 
