@@ -29,6 +29,17 @@ p*ps+ps-1, lowest free pages first, a page is freed whole); a request's
 tokens that do not fill a page stay with the request (its last page, which
 later tokens continue) and are not inserted.
 
+Two-tier variant, same page, section "What the C++ tree is actually for": a
+host tier of slots beside the device pool; a node is on the device, on the
+host or both; a match reports the device part and the host part with a node
+per tier; writes to the host and loads back are transactions resolved by a
+later commit (only the write's commit carries a success flag); device
+eviction counts device-resident children only.  Readings for it: page size 1;
+a write-through covers the root path and locks it until the commit; a device
+leaf with a committed host copy leaves the device only, one without leaves the
+tree with its host-only subtree; host eviction drops host-only leaves in the
+device order; an insert over a host-only node gives it the caller's slots.
+
 Readings where the pages are silent (each listed in the design notes):
 page_size 1 unless asked; a logical clock that ticks once per match/insert call and
 stamps every node the call visits; heap key (priority, last_access, node id)
