@@ -318,6 +318,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--host-tier", action="store_true",
+                    help="only run the host tier's copy measurement (write-through and load back)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path has no cross-GPU step); "
@@ -333,6 +335,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
+    if args.host_tier:
+        print(json.dumps(host_tier_extra()), flush=True)
         return
     print(f"[bench] setup config {args.config}", file=sys.stderr, flush=True)
     st = setup(args.config)

@@ -756,11 +756,10 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
   }
 }
 
-// Iterations [t_begin, t_end), t_begin >= 1: sprev holds S(t-1) in VGPRs on entry and
-// S(t_end-1) on exit.
-// Iterations [t_begin, t_end).  On entry kf holds K(t_begin) and vf V(t_begin - 1); each
-// iteration reads the next ones at its end, after its MFMAs are issued, so their LDS
-// latency overlaps the matrix work instead of delaying the next iteration's first MFMA.
+// Iterations [t_begin, t_end), t_begin >= 1.  On entry sprev holds S(t_begin - 1) in VGPRs,
+// kf K(t_begin) and vf V(t_begin - 1); on exit sprev holds S(t_end - 1).  Each iteration reads
+// the next K and V at its end, after its MFMAs are issued, so their LDS latency overlaps the
+// matrix work instead of delaying the next iteration's first MFMA.
 template <int D, bool MASK, bool TRACK>
 __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
                                           const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[2],
@@ -782,9 +781,7 @@ __device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, con
   }
 }
 
-// One pass over keys [0, k1).  first_pass: the references come from tile 0's row maxima;
-// otherwise es.mc is already set.
-// One pass over the keys.  first_pass: each row's reference point is its maximum over
+// One pass over keys [0, k1).  first_pass: each row's reference point is its maximum over
 // tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
 template <int D, bool TRACK>
 __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
