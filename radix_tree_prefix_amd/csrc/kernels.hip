@@ -434,7 +434,10 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 // Extend engine.  Each wave owns 64 query rows as two 32-row blocks, and every K and V
 // operand it reads from LDS feeds the MFMAs of both blocks, so LDS reads per flop are
 // half those of a 32-row wave.  A workgroup is 4 waves (256 rows) and a CU holds one: each
-// wave has a SIMD and up to 512 registers to itself.  The Q fragments and the O
+// wave has a SIMD and up to 512 registers to itself.  The draft-tree verify instantiation
+// gives each wave one 32-row block (128 rows per workgroup): its few verify tokens per
+// request would leave half of a 256-row workgroup empty, and the empty rows would still
+// cost their matrix and vector work.  The Q fragments and the O
 // accumulators stay in AGPRs (only MFMAs touch them in the loop); the scores, weights and
 // addresses use the VGPRs.
 //
@@ -459,23 +462,26 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 // does not depend on the reference point.
 constexpr int kExtKB = 32;           // keys per tile
 constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
-constexpr int kExtRows = 256;        // query rows per workgroup: 4 waves x 64
-constexpr int kExtWaves = kExtRows / 64;
+constexpr int kExtWaves = 4;         // waves per workgroup, one per SIMD
+constexpr int kExtRows = 256;        // query rows per workgroup of the causal kernel: 4 waves x 64
+constexpr int kVerifyRows = 128;     // of the draft-tree verify kernel: 4 waves x 32
 constexpr int kExtAhead = kExtNS - 2;            // tiles in flight ahead of the math
 constexpr int kExtSlotLead = 2 * kExtAhead + 1;  // slot ids are loaded this many tiles ahead
 constexpr int kExtRing = 16;                     // slot-id ring entries (tiles)
 static_assert(kExtRing >= kExtSlotLead && kExtRing > kExtAhead, "slot ring too small");
 
-template <int D>
+// RB: 32-row blocks per wave (2 in the causal kernel, 1 in the verify kernel).
+template <int D, int RB>
 struct ExtState {
-  f32x16 o[2][D / 32];          // O^T per row block (layout as WaveState)
-  float mc[2];                  // reference point times c, per row block (fixed per pass)
-  float mx[2];                  // this lane's running maximum of raw scores (tracking pass)
-  float l[2];                   // this lane's halves of the running sums
+  f32x16 o[RB][D / 32];         // O^T per row block (layout as WaveState)
+  float mc[RB];                 // reference point times c, per row block (fixed per pass)
+  float mx[RB];                 // this lane's running maximum of raw scores (tracking pass)
+  float l[RB];                  // this lane's halves of the running sums
 };
 
-struct Weights2 {
-  uint4 p[2][kExtKB / 16];      // [row block][16-key step]: P^T in bf16 pairs
+template <int RB>
+struct ExtWeights {
+  uint4 p[RB][kExtKB / 16];      // [row block][16-key step]: P^T in bf16 pairs
 };
 
 // Per-lane LDS byte offsets of the MFMA operands within a stage: K chunk of step ks for
@@ -520,17 +526,17 @@ __device__ __forceinline__ KFrags<D> ext_read_k(const char* kst, const ExtOffset
 }
 
 // S^T of both row blocks (results in the MFMA's accumulation registers).
-template <int D>
-__device__ __forceinline__ void ext_qk(f32x16 (&sc)[2], const KFrags<D>& kf, const bf16x8 (&qf)[2][D / 16]) {
+template <int D, int RB>
+__device__ __forceinline__ void ext_qk(f32x16 (&sc)[RB], const KFrags<D>& kf, const bf16x8 (&qf)[RB][D / 16]) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) sc[rb][j] = 0.f;
   }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
       sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[ks], qf[rb][ks], sc[rb], 0, 0, 0);
 }
 
@@ -546,11 +552,11 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 
 // Weights P = bf16(exp2(S*c - m*c)) of both row blocks and their row sums (of the bf16
 // weights, as the second MFMA sees them); TRACK: also the running maxima of the scores.
-template <int D, bool TRACK>
-__device__ __forceinline__ void ext_weights(Weights2& w, ExtState<D>& es, const f32x16 (&sc)[2], float c) {
+template <int D, int RB, bool TRACK>
+__device__ __forceinline__ void ext_weights(ExtWeights<RB>& w, ExtState<D, RB>& es, const f32x16 (&sc)[RB], float c) {
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     if (TRACK) es.mx[rb] = fmaxf(es.mx[rb], max16(sc[rb]));
     float sum = 0.f;
 #pragma unroll
@@ -597,14 +603,14 @@ __device__ __forceinline__ VFrags<D> ext_read_v(const char* vst, const ExtOffset
 }
 
 // O^T += V^T P^T for both row blocks.
-template <int D>
-__device__ __forceinline__ void ext_pv(ExtState<D>& es, const VFrags<D>& vf, const Weights2& w) {
+template <int D, int RB>
+__device__ __forceinline__ void ext_pv(ExtState<D, RB>& es, const VFrags<D>& vf, const ExtWeights<RB>& w) {
 #pragma unroll
   for (int kstep = 0; kstep < kExtKB / 16; ++kstep)
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
         es.o[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.a[kstep][mb], __builtin_bit_cast(bf16x8, w.p[rb][kstep]),
                                                                es.o[rb][mb], 0, 0, 0);
 }
@@ -724,10 +730,10 @@ __device__ __forceinline__ void ext_wait_next(int t) {
 
 // Scores of tile t to VGPRs (the next iteration's operand) and, for MASK, -inf past this
 // lane's last visible key or the tile's last key.
-template <int D, bool MASK>
-__device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (&src)[2], const ExtStream<D>& a, int t) {
+template <int D, int RB, bool MASK>
+__device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[RB], const f32x16 (&src)[RB], const ExtStream<D>& a, int t) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     dst[rb] = src[rb];
     asm volatile("" : "+v"(dst[rb]));
   }
@@ -735,7 +741,7 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
     const int key0 = t * kExtKB;
     const int nk = min(kExtKB, a.k1 - key0);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       const int thr = min(a.lim[rb] - key0, nk - 1) - a.hik;
       if (a.tree) {
         // key k = key0 + hik + ext_key(j): causal bound as above, and past tree_base only
@@ -760,32 +766,32 @@ __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[2], const f32x16 (
 // kf K(t_begin) and vf V(t_begin - 1); on exit sprev holds S(t_end - 1).  Each iteration reads
 // the next K and V at its end, after its MFMAs are issued, so their LDS latency overlaps the
 // matrix work instead of delaying the next iteration's first MFMA.
-template <int D, bool MASK, bool TRACK>
-__device__ __forceinline__ void ext_iters(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
-                                          const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[2],
+template <int D, int RB, bool MASK, bool TRACK>
+__device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
+                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[RB],
                                           KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
   for (int t = t_begin; t < t_end; ++t) {
     ext_wait_next<D>(t);
     const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, t + kExtAhead);
     ext_slot_dma<D>(sh, a, t + kExtSlotLead);
     ext_kv_dma<D>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
-    f32x16 scur[2];
-    ext_qk<D>(scur, kf, qf);
-    Weights2 w;
-    ext_weights<D, TRACK>(w, es, sprev, a.c);
-    ext_pv<D>(es, vf, w);
+    f32x16 scur[RB];
+    ext_qk<D, RB>(scur, kf, qf);
+    ExtWeights<RB> w;
+    ext_weights<D, RB, TRACK>(w, es, sprev, a.c);
+    ext_pv<D, RB>(es, vf, w);
     kf = ext_read_k<D>(sh.st[(t + 1) % kExtNS].k, off);
     vf = ext_read_v<D>(sh.st[t % kExtNS].v, off);
-    ext_take_scores<D, MASK>(sprev, scur, a, t);
+    ext_take_scores<D, RB, MASK>(sprev, scur, a, t);
     __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
   }
 }
 
 // One pass over keys [0, k1).  first_pass: each row's reference point is its maximum over
 // tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
-template <int D, bool TRACK>
-__device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
-                                         const bf16x8 (&qf)[2][D / 16], const ExtStream<D>& a, bool first_pass) {
+template <int D, int RB, bool TRACK>
+__device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
+                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D>& a, bool first_pass) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
   const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
   // prologue: slot ids of the first tiles, then their K/V
@@ -795,47 +801,47 @@ __device__ __forceinline__ void ext_pass(ExtState<D>& es, ExtShared<D>& sh, cons
   // tile 0: its scores only
   ext_wait<D>(0);
   ext_slot_dma<D>(sh, a, kExtSlotLead);
-  f32x16 sprev[2];
+  f32x16 sprev[RB];
   KFrags<D> kf;
   VFrags<D> vf;
   {
     const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, kExtAhead);
     kf = ext_read_k<D>(sh.st[0].k, off);
     ext_kv_dma<D>(sh.st[kExtAhead % kExtNS], a, sl);
-    f32x16 scur[2];
-    ext_qk<D>(scur, kf, qf);
+    f32x16 scur[RB];
+    ext_qk<D, RB>(scur, kf, qf);
     // every prologue tile has landed (the wait above counted to zero): tile 1's K and
     // tile 0's V for the first iteration
     kf = ext_read_k<D>(sh.st[1 % kExtNS].k, off);
     vf = ext_read_v<D>(sh.st[0].v, off);
-    if (t_mask == 0) ext_take_scores<D, true>(sprev, scur, a, 0);
-    else ext_take_scores<D, false>(sprev, scur, a, 0);
+    if (t_mask == 0) ext_take_scores<D, RB, true>(sprev, scur, a, 0);
+    else ext_take_scores<D, RB, false>(sprev, scur, a, 0);
   }
   if (first_pass) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       float m = max16(sprev[rb]);
       m = fmaxf(m, __shfl_xor(m, 32));
       es.mc[rb] = (m == -INFINITY ? 0.f : m) * a.c;
     }
   }
   const int t_split = max(1, t_mask);
-  ext_iters<D, false, TRACK>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
-  ext_iters<D, true, TRACK>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
+  ext_iters<D, RB, false, TRACK>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
+  ext_iters<D, RB, true, TRACK>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
   // the last tile's weights and P.V (vf holds its V)
-  Weights2 w;
-  ext_weights<D, TRACK>(w, es, sprev, a.c);
-  ext_pv<D>(es, vf, w);
+  ExtWeights<RB> w;
+  ext_weights<D, RB, TRACK>(w, es, sprev, a.c);
+  ext_pv<D, RB>(es, vf, w);
   // the loads past the last tile have landed, and every wave is done with the stages and
   // the ring, before a later pass refills them or the workgroup ends
   wait_vmcnt_barrier<0>();
 }
 
 // Zero O and l; no maximum seen yet.
-template <int D>
-__device__ __forceinline__ void ext_reset(ExtState<D>& es) {
+template <int D, int RB>
+__device__ __forceinline__ void ext_reset(ExtState<D, RB>& es) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -848,13 +854,13 @@ __device__ __forceinline__ void ext_reset(ExtState<D>& es) {
 // Write the valid rows' outputs O / l (bf16).  Returns true if any of them, or l, is not
 // finite: only an overflow of the weights makes that happen (x * 0 is 0 for finite x and
 // NaN for inf or NaN, so z is NaN exactly then).
-template <int D>
-__device__ __forceinline__ bool ext_store(const ExtState<D>& es, const bool (&valid)[2], const int64_t (&qrow_idx)[2],
+template <int D, int RB>
+__device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool (&valid)[RB], const int64_t (&qrow_idx)[RB],
                                           uint16_t* __restrict__ out, int lane) {
   const int hi = lane >> 5;
   float z = 0.f;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     if (!valid[rb]) continue;
     const float l = xhalf_sum(es.l[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -888,12 +894,15 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
     int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out, int uniform_n,
     const uint64_t* __restrict__ tree_mask) {
-  static_assert(kThreads == 64 * kExtWaves, "one wave per 64 rows");
+  static_assert(kThreads == 64 * kExtWaves, "one wave per SIMD");
+  constexpr int RB = TREE ? 1 : 2;                // 32-row blocks per wave
+  constexpr int kRows = kExtWaves * 32 * RB;
+  static_assert(kRows == (TREE ? kVerifyRows : kExtRows), "rows per workgroup as the launchers assume");
   __shared__ ExtShared<D> sh;
   using L = StageLayout<D, kExtKB>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
-  const int tpb = kExtRows / G;                   // tokens per tile
+  const int tpb = kRows / G;                      // tokens per tile
   const int kvh = blockIdx.x % Hkv;
   const int rest = blockIdx.x / Hkv;
   // requests in the given order; within a request the later (longer) q-tiles first
@@ -909,12 +918,12 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
   ExtStream<D> a;
   a.tree = TREE;
   a.tree_base = prefix;
-  bf16x8 qf[2][D / 16];
-  int64_t qrow_idx[2];
-  bool valid[2];
+  bf16x8 qf[RB][D / 16];
+  int64_t qrow_idx[RB];
+  bool valid[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = wave * 64 + rb * 32 + (lane & 31);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave * 32 * RB + rb * 32 + (lane & 31);
     const int t = row / G, g = row % G;
     valid[rb] = row < tpb * G && t < ntok;
     qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
@@ -938,29 +947,31 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
   a.mask_from = a.tree ? prefix : prefix + t0 + 1;   // keys below this are visible to every row
   a.c = sm_scale * kLog2e;
   const ExtOffsets<D> off = ext_offsets<D>(lane);
-  ExtState<D> es;
-  ext_reset<D>(es);
+  ExtState<D, RB> es;
+  ext_reset<D, RB>(es);
   // Q fragments and O accumulators live in AGPRs through the loop: only MFMAs read
   // them there, which leaves the VGPRs to the scores, weights and addresses.
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[rb][ks]));
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
   for (int pass = 0;; ++pass) {
-    ext_pass<D, false>(es, sh, off, qf, a, pass == 0);
-    const bool overflow = ext_store<D>(es, valid, qrow_idx, out, lane);
+    ext_pass<D, RB, false>(es, sh, off, qf, a, pass == 0);
+    const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
     if (pass == 1 || !__syncthreads_or(overflow)) break;
     // Some weight overflowed: find each row's true maximum, then recompute the rows
     // with it as the reference (the outputs above are overwritten).
-    ext_reset<D>(es);
-    ext_pass<D, true>(es, sh, off, qf, a, true);
-    const float mx0 = xhalf_max(es.mx[0]), mx1 = xhalf_max(es.mx[1]);
-    ext_reset<D>(es);
-    es.mc[0] = (mx0 == -INFINITY ? 0.f : mx0) * a.c;
-    es.mc[1] = (mx1 == -INFINITY ? 0.f : mx1) * a.c;
+    ext_reset<D, RB>(es);
+    ext_pass<D, RB, true>(es, sh, off, qf, a, true);
+    float mx[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
+    ext_reset<D, RB>(es);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) es.mc[rb] = (mx[rb] == -INFINITY ? 0.f : mx[rb]) * a.c;
   }
 }
 
@@ -1390,7 +1401,7 @@ int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_po
   if (!q || !k_pool || !v_pool || !req_to_token || !prefix_lens || !tree_mask || !out)
     return rs::fail(RS_E_INVAL, "rs_tree_verify_attention: null pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = Hq / Hkv, tpb = kExtRows / G;
+  const int G = Hq / Hkv, tpb = kVerifyRows / G;
   const int n_qtiles = (n + tpb - 1) / tpb;
   const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
   if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_tree_verify_attention: grid too large");
