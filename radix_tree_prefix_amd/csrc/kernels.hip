@@ -448,9 +448,9 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 //
 // The loop is software-pipelined by one tile so that one wave overlaps its own matrix
 // and vector work.  Iteration t: S(t) = K(t) Q^T runs on the matrix cores while the VALU
-// turns S(t-1) into weights; then O += V(t-1)^T P(t-1); then S(t) moves from the MFMA
-// result registers to VGPRs (the copy is the pipeline's buffer swap) and, on the causal
-// diagonal or a ragged end, is masked.
+// turns S(t-1) into weights; then O += V(t-1)^T P(t-1), among whose MFMAs S(t) moves from
+// the MFMA result registers to VGPRs (the copy is the pipeline's buffer swap); on the causal
+// diagonal or a ragged end it is then masked.
 //
 // Softmax reference.  Each row's reference point is the maximum of its scores in tile 0
 // and stays fixed for the pass, so the loop never rescales O and tracks no maximum.
@@ -728,15 +728,13 @@ __device__ __forceinline__ void ext_wait_next(int t) {
   else wait_vmcnt_barrier<0>();
 }
 
-// Scores of tile t to VGPRs (the next iteration's operand) and, for MASK, -inf past this
-// lane's last visible key or the tile's last key.
+// Scores of tile t to the next iteration's operand and, for MASK, -inf past this lane's last
+// visible key or the tile's last key.  The copy from the MFMA result registers is left to the
+// scheduler, which spreads it among the P.V MFMAs.
 template <int D, int RB, bool MASK>
 __device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[RB], const f32x16 (&src)[RB], const ExtStream<D>& a, int t) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    dst[rb] = src[rb];
-    asm volatile("" : "+v"(dst[rb]));
-  }
+  for (int rb = 0; rb < RB; ++rb) dst[rb] = src[rb];
   if (MASK) {
     const int key0 = t * kExtKB;
     const int nk = min(kExtKB, a.k1 - key0);
