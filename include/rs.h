@@ -201,14 +201,15 @@ int rs_match_prefix2(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_
 
 /* Write-through: host slots for every node on node's root path that has no host copy (the
  * path must be on the device), evicting host-only leaves, least recently used first, to
- * fit (RS_E_NOSPACE if it cannot: what was evicted stays evicted, nothing else changes).  Writes the (device slot, host slot)
+ * fit (RS_E_NOSPACE if it cannot: what was evicted stays evicted, nothing else changes; a path
+ * longer than the whole tier fails before anything is evicted).  Writes the (device slot, host slot)
  * pairs to copy, *out_n of them (host arrays of capacity cap), and a ticket; the path stays
  * locked and the copies count as in flight until rs_commit(ticket). */
 int rs_write_through(rs_tree* t, int64_t node, int64_t cap, int32_t* out_dev_slots,
                      int32_t* out_host_slots, int64_t* out_n, int64_t* out_ticket);
 
 /* Load back: device slots (rs_alloc_slots rules, evicting to fit; RS_E_NOSPACE: what was
- * evicted stays evicted, nothing else changes) for every node on node's root path that is on the host only; writes the (host slot,
+ * evicted stays evicted, nothing else changes; more than the whole pool fails before evicting) for every node on node's root path that is on the host only; writes the (host slot,
  * device slot) pairs to copy and a ticket; the path stays locked until rs_commit(ticket). */
 int rs_load_back(rs_tree* t, int64_t node, int64_t cap, int32_t* out_host_slots,
                  int32_t* out_dev_slots, int64_t* out_n, int64_t* out_ticket);

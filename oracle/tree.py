@@ -380,6 +380,8 @@ class RadixTree:
         assert all(len(nd.value) for nd in path), "write-through of a node not on the device"
         todo = [nd for nd in path if not len(nd.host) and nd.pend == 0]
         need = sum(len(nd.key) for nd in todo)
+        if need > self.host_slots:                # can never fit: fail before evicting anything
+            raise NoSpace(need)
         got = self._alloc_host(need)
         t = self.next_ticket
         self.next_ticket += 1
@@ -400,6 +402,8 @@ class RadixTree:
         (host slots, device slots, ticket); the path stays locked until commit."""
         path = self.path(nid)
         todo = [nd for nd in path if not len(nd.value)]
+        if sum(len(nd.key) for nd in todo) > self.pool_slots:   # can never fit
+            raise NoSpace(sum(len(nd.key) for nd in todo))
         self.inc_lock_ref(nid)
         try:
             got = self.alloc(sum(len(nd.key) for nd in todo))

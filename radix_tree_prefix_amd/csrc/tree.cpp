@@ -614,6 +614,9 @@ int rs_write_through(rs_tree* t, int64_t node, int64_t cap, int32_t* out_dev_slo
       need += int64_t(x->key.size());
     }
   }
+  if (need > t->host->capacity())
+    return rs::fail(RS_E_NOSPACE, "rs_write_through: " + std::to_string(need) + " tokens, host tier of " +
+                                      std::to_string(t->host->capacity()) + " slots");
   if (need > cap) return rs::fail(RS_E_INVAL, "rs_write_through: " + std::to_string(need) + " pairs, capacity " +
                                                   std::to_string(cap));
   std::vector<int32_t> got(size_t(need) + 1);
@@ -652,6 +655,9 @@ int rs_load_back(rs_tree* t, int64_t node, int64_t cap, int32_t* out_host_slots,
       todo.push_back(x);
       need += int64_t(x->key.size());
     }
+  if (need > t->alloc.capacity())
+    return rs::fail(RS_E_NOSPACE, "rs_load_back: " + std::to_string(need) + " tokens, pool of " +
+                                      std::to_string(t->alloc.capacity()) + " slots");
   if (need > cap) return rs::fail(RS_E_INVAL, "rs_load_back: " + std::to_string(need) + " pairs, capacity " +
                                                   std::to_string(cap));
   t->lock(nd);

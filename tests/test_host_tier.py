@@ -321,3 +321,39 @@ def test_host_tier_rejects_pages():
     t = rs.Tree(64, 4)
     with pytest.raises(rs.RsError):
         t.enable_host(64)
+
+
+def test_error_paths():
+    """Calls out of sequence fail with an error and change nothing."""
+    t = rs.Tree(16)
+    with pytest.raises(rs.RsError):
+        t.evict_host(1)                            # tier off
+    with pytest.raises(rs.RsError):
+        t.enable_host(0)
+    t.enable_host(8)
+    with pytest.raises(rs.RsError):
+        t.enable_host(8)                           # at most once
+    with pytest.raises(rs.RsError):
+        t.commit(12345, True)                      # unknown ticket
+    with pytest.raises(rs.StaleError):
+        t.write_through(999)                       # no such node
+    assert t.match2(np.zeros(0, np.int32))[2:] == (0, 0, 0, 0)
+    _row, node, _m = _admit(t, np.array([4, 5, 6], np.int32))
+    before = t.dump()
+    t2 = rs.Tree(16)
+    t2.enable_host(2)
+    _r2, n2, _m2 = _admit(t2, np.array([4, 5, 6], np.int32))
+    before2 = t2.dump()
+    with pytest.raises(rs.NoSpaceError):
+        t2.write_through(n2)                       # 3 tokens never fit 2 host slots
+    assert t2.dump() == before2
+    s, d, tk = t.load_back(node)                   # already on the device: nothing to copy
+    assert len(s) == len(d) == 0
+    t.commit(tk, True)
+    assert t.dump() == before
+    _d, _h, tk = t.write_through(node)
+    _d2, _h2, tk2 = t.write_through(node)          # in flight: nothing new to back up
+    assert len(_d2) == 0 and tk2 != tk
+    t.commit(tk2, True)
+    t.commit(tk, True)
+    assert t.stats()["host_tokens"] == 3 and t.stats()["host_free"] == 5
