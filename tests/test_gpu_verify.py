@@ -66,7 +66,7 @@ def _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed, chain=False):
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,n", [(8, 2, 128, 1), (8, 2, 128, 16), (64, 8, 128, 5), (64, 8, 128, 64),
-                                        (32, 8, 64, 33)])
+                                        (32, 8, 64, 33), (128, 8, 128, 17), (8, 8, 64, 64)])
 def test_tree_verify_against_oracle(torch_rs, Hq, Hkv, D, n):
     torch, rs = torch_rs
     prefixes = [0, 37, 1000]
