@@ -3,14 +3,19 @@
 
 One step = one pass of the device path over a resident batch: store the new
 tokens' K/V into their pool slots, extend attention for the extend requests,
-prefix-aware decode attention (plan-driven, fused LSE merge) for the decode
-requests.  The host tree admission, table build and plan build that produce
+prefix-aware decode attention (plan-driven work items, then a log-sum-exp merge
+kernel) for the decode requests.  The host tree admission, table build and plan build that produce
 the batch are timed separately and reported (`host_ms`).
 
 Default workload: the large mixed batch (128 x 512-token extends + 128 decodes,
 contexts 1k-32k, GQA 64/8, d128, bf16, 4M-slot pool).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline] [--no-extra]
+                    [--flush]
+
+--flush overwrites a 1 GiB buffer before every timed step, so that a workload small enough
+to stay in L2 and the 256 MB MALL between steps is read from HBM each time; the step time
+is then the sum of the per-kernel event times (the flush itself is not counted).
 """
 from __future__ import annotations
 
@@ -316,10 +321,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel runs of the other configs")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite 1 GiB before every timed step (for workloads that fit in the caches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--host-tier", action="store_true",
                     help="only run the host tier's copy measurement (write-through and load back)")
+    ap.add_argument("--verify", action="store_true",
+                    help="only run the draft-tree verify measurement (cache-flushed)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path has no cross-GPU step); "
@@ -339,6 +348,9 @@ def main():
     if args.host_tier:
         print(json.dumps(host_tier_extra()), flush=True)
         return
+    if args.verify:
+        print(json.dumps(verify_extra(make_flush())), flush=True)
+        return
     print(f"[bench] setup config {args.config}", file=sys.stderr, flush=True)
     st = setup(args.config)
     print(f"[bench] setup done in {st.host_s:.1f}s (history {st.history_s:.2f}s, admit {st.admit_s:.3f}s)",
@@ -350,8 +362,11 @@ def main():
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    flush = make_flush() if args.flush else None
     t0 = time.perf_counter()
     for e in ev:
+        if flush is not None:
+            flush()
         e[0].record()
         run_store(st)
         e[1].record()
@@ -365,6 +380,8 @@ def main():
     ext_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     store_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    if flush is not None:            # the flushes sit between the steps: count the kernels only
+        ms_step = store_ms + ext_ms + dec_ms
     tokens = (st.ext_tokens if st.ext else 0) + len(st.dec)
     value = tokens / (ms_step / 1e3)
 
@@ -421,7 +438,7 @@ def extra_configs():
     import torch
     res = {}
     flush = make_flush()
-    for cfg in (2, 4, 3):
+    for cfg in (2, 4, 3, 1):
         print(f"[bench] extra config {cfg}", file=sys.stderr, flush=True)
         st = setup(cfg)
         d = {"workload": st.wl.name}
@@ -436,9 +453,13 @@ def extra_configs():
         if st.ext:
             med, _ = time_fn(lambda: run_extend(st), 20, 3, flush)
             f = extend_flops(st)
-            d.update({"extend_us": round(med * 1e3, 2), "flops": f, "tflops": round(f / (med / 1e3) / 1e12, 2),
-                      "mfma_frac": round(f / (med / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            tf = f / (med / 1e3) / 1e12
+            d.update({"extend_us": round(med * 1e3, 2), "flops": f, "tflops": round(tf, 2),
                       "tokens_per_s": round(st.ext_tokens / (med / 1e3), 1)})
+            if st.wl.dtype == "bf16":
+                d["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+            else:                    # the fp32 path is a VALU kernel: against the fp32 vector peak
+                d["fp32_frac"] = round(tf / FP32_PEAK_TFLOPS, 4)
         res[str(cfg)] = d
         del st
         torch.cuda.empty_cache()

@@ -194,7 +194,9 @@ int rs_host_tier_enable(rs_tree* t, int64_t host_slots);
 /* Like rs_match_prefix, continued through nodes that are on the host only (split and
  * touched the same way): *out_dev_len tokens are on the device (slots in out_dev_slots,
  * node *out_dev_node), *out_len in total; out_host_slots receives the host slots of
- * positions *out_dev_len .. *out_len-1, *out_node is the node the match ends at. */
+ * positions *out_dev_len .. *out_len-1, *out_node is the node the match ends at.
+ * Needs the host tier (RS_E_INVAL if it is off) and page size 1 (RS_E_UNSUPPORTED
+ * otherwise); a refused call leaves the tree unchanged. */
 int rs_match_prefix2(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_dev_slots,
                      int32_t* out_host_slots, int64_t* out_dev_len, int64_t* out_len,
                      int64_t* out_dev_node, int64_t* out_node);
@@ -386,7 +388,10 @@ int rs_copy_kv(void* dst_k, void* dst_v, const void* src_k, const void* src_v, c
  *   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
  * plan = NULL: each request is one segment (flat).  ws: device workspace of at least
  * rs_decode_workspace_bytes.  Launches that share a workspace must not overlap.
- * fp32 runs the flat path (plan ignored). */
+ * fp32 runs the flat path (plan ignored).  max_seq_len must be >= every seq_lens[b] and
+ * <= ld (RS_E_INVAL if ld is smaller); the device cannot check seq_lens, so without a plan
+ * a request longer than max_seq_len is cut to its first max_seq_len keys rather than read
+ * out of bounds (a plan carries the key ranges it was built with). */
 int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
                         int32_t B, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D,

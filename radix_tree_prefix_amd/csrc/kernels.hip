@@ -974,7 +974,7 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
 }
 
 // ------------------------------------------------------------------ decode (bf16)
-// Decode: 64-key tiles, two stages, two workgroups per CU (as extend).
+// Decode: 64-key tiles, two stages, up to two workgroups per CU.
 constexpr int kDecKB = 64, kDecNS = 2;
 struct DecodeArgs {
   const uint16_t* q;
@@ -985,6 +985,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const int32_t* plan;        // device image, or nullptr for the flat mode
   int flat_nch;               // flat mode: chunks per request
+  int max_seq;                // flat mode: keys are read up to min(seq_lens[b], max_seq) only
   int Hq, Hkv;
   float sm_scale;
   float* o_part;              // [Hkv][P][G][D]
@@ -1012,7 +1013,8 @@ __device__ __forceinline__ PartList part_list(const DecodeArgs& a, int b) {
   } else {
     pl.list = nullptr;
     pl.base = b * a.flat_nch;
-    pl.n = (a.seq_lens[b] + rs::kFlatChunk - 1) / rs::kFlatChunk;
+    // a request longer than max_seq is cut to it, so its partials stay in its own range
+    pl.n = (min(a.seq_lens[b], a.max_seq) + rs::kFlatChunk - 1) / rs::kFlatChunk;
   }
   return pl;
 }
@@ -1034,7 +1036,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   } else {
     const int b = item / a.flat_nch, ch = item % a.flat_nch;
     k0 = ch * rs::kFlatChunk;
-    k1 = min(k0 + rs::kFlatChunk, a.seq_lens[b]);
+    k1 = min(k0 + rs::kFlatChunk, min(a.seq_lens[b], a.max_seq));
     if (k0 >= k1) return;
     rep = b; nreq = 1; part_base = item;
   }
@@ -1204,8 +1206,8 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens,
-    const int32_t* __restrict__ seq_lens, int max_q, int Hq, int Hkv, float sm_scale, float* __restrict__ out,
-    float* __restrict__ lse_out) {
+    const int32_t* __restrict__ seq_lens, int max_q, int max_len, int Hq, int Hkv, float sm_scale,
+    float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int DPL = D / 64;                    // output dims per lane
   __shared__ float qs[D];
   const int lane = threadIdx.x;
@@ -1214,7 +1216,7 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
   const int i = rest % max_q, b = rest / max_q;
   int pos, qrow;
   if (seq_lens) {
-    pos = seq_lens[b] - 1;
+    pos = min(seq_lens[b], max_len) - 1;      // decode: a request is cut to max_len keys
     qrow = b;
   } else {
     if (i >= extend_lens[b]) return;
@@ -1445,7 +1447,7 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
     hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64), 0, s, static_cast<const float*>(q),
                        static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
-                       qo_indptr, prefix_lens, extend_lens, nullptr, max_extend_len, Hq, Hkv, sm_scale,
+                       qo_indptr, prefix_lens, extend_lens, nullptr, max_extend_len, 0, Hq, Hkv, sm_scale,
                        static_cast<float*>(out), nullptr);
     return hip_check("rs_extend_attention");
   }
@@ -1457,6 +1459,7 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
                         float sm_scale, int32_t dtype, const rs_plan* plan, const void* plan_dev, void* ws,
                         int64_t ws_bytes, void* out, float* lse_out, void* stream) {
   if (B < 0 || max_seq_len < 0 || ld <= 0) return rs::fail(RS_E_INVAL, "rs_decode_attention: bad sizes");
+  if (ld < max_seq_len) return rs::fail(RS_E_INVAL, "rs_decode_attention: table rows shorter than max_seq_len");
   if (!dims_ok(Hq, Hkv, D)) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: heads/head_dim unsupported");
   if (B == 0) return RS_OK;
   if (!q || !k_pool || !v_pool || !req_to_token || !seq_lens || !out)
@@ -1467,7 +1470,8 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
     auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
     hipLaunchKernelGGL(kern, dim3(unsigned(int64_t(B) * Hq)), dim3(64), 0, s, static_cast<const float*>(q),
                        static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
-                       nullptr, nullptr, nullptr, seq_lens, 1, Hq, Hkv, sm_scale, static_cast<float*>(out), lse_out);
+                       nullptr, nullptr, nullptr, seq_lens, 1, max_seq_len, Hq, Hkv, sm_scale,
+                       static_cast<float*>(out), lse_out);
     return hip_check("rs_decode_attention");
   }
   if (dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: dtype");
@@ -1499,6 +1503,7 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
   a.seq_lens = seq_lens;
   a.plan = static_cast<const int32_t*>(plan_dev);
   a.flat_nch = flat_nch;
+  a.max_seq = max_seq_len;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.sm_scale = sm_scale;

@@ -565,6 +565,10 @@ int rs_match_prefix2(rs_tree* t, const int32_t* tokens, int64_t n, int32_t* out_
   if (!t || n < 0 || (n && (!tokens || !out_dev_slots || !out_host_slots)) || !out_dev_len || !out_len ||
       !out_dev_node || !out_node)
     return rs::fail(RS_E_INVAL, "rs_match_prefix2: bad arguments");
+  // the two-tier walk compares and splits one token at a time: page size 1 only, which is
+  // also the only size the host tier is enabled at
+  if (t->ps != 1) return rs::fail(RS_E_UNSUPPORTED, "rs_match_prefix2: page size 1 only");
+  if (!t->host) return rs::fail(RS_E_INVAL, "rs_match_prefix2: the host tier is off");
   RS_GUARD_BEGIN
   ++t->clock;
   ++t->match_calls;

@@ -28,3 +28,31 @@ def read_golden(name):
             else:
                 out[k] = [v] if k in ("request", "expect") else v
     return out
+
+
+# Per-request bounds of the bf16 parity checks.  Max-abs 2e-2 is the stated tolerance for
+# bf16 outputs.  At 32k-token contexts the outputs themselves are only ~0.04 in magnitude,
+# so that bound alone cannot see a lost chunk of keys; the relative RMS bound
+# ||got - ref|| / ||ref|| <= 1e-2 scales with the request's own outputs.  A correct bf16
+# computation (fp32 scores, bf16 weights, bf16 output) lands near 2.3e-3 on every context
+# length of the mixed batch, while dropping a single 32-key tile of a 32k context moves the
+# output by 2.8e-2 or more (test_parity_bound.py holds both as a CPU control).
+BF16_MAX_ABS = 2e-2
+BF16_REL_RMS = 1e-2
+LSE_MAX_ABS = 1e-2
+
+
+def bf16_request_errors(got, ref):
+    """(max-abs error, relative RMS error) of one request's outputs against the oracle's."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    den = float(np.sqrt((ref * ref).sum()))
+    rel = float(np.sqrt((d * d).sum())) / den if den > 0 else float(np.sqrt((d * d).sum()))
+    return float(np.abs(d).max()) if d.size else 0.0, rel
+
+
+def bf16_request_ok(got, ref):
+    mx, rel = bf16_request_errors(got, ref)
+    return mx <= BF16_MAX_ABS and rel <= BF16_REL_RMS

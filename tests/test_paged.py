@@ -218,3 +218,27 @@ def test_page_size_must_divide_the_pool():
         rs.Tree(10, 4)
     with pytest.raises(rs.RsError):
         rs.Tree(10, 0)
+
+
+def test_two_tier_match_refuses_a_paged_tree():
+    """The two-tier match walks one token at a time, so it needs page size 1 (the only size
+    the host tier runs at): on a page-4 tree it is refused and changes nothing.  Without the
+    refusal it would split inside a page and read past the caller's tokens."""
+    t = rs.Tree(16, 4)
+    row, node, _m = t.admit(np.arange(8, dtype=np.int32), 8, 0)
+    before_dump, before_stats = t.dump(), t.stats()
+    with pytest.raises(rs.RsError) as e:
+        t.match2(np.arange(6, dtype=np.int32))
+    assert e.value.code == rs._lib.RS_E_UNSUPPORTED
+    assert t.dump() == before_dump and t.stats() == before_stats
+    t.dec_lock_ref(node)
+
+
+def test_two_tier_match_needs_the_host_tier():
+    t = rs.Tree(16)
+    t.admit(np.arange(8, dtype=np.int32), 8, 0)
+    before = t.dump()
+    with pytest.raises(rs.RsError) as e:
+        t.match2(np.arange(6, dtype=np.int32))
+    assert e.value.code == rs._lib.RS_E_INVAL
+    assert t.dump() == before
