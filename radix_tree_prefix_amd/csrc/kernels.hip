@@ -78,13 +78,13 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // * 16-byte chunks: chunk c of LDS row R sits at position c ^ swz(R), which spreads the
 //   16 rows of a K-operand ds_read_b128 phase and the 4 rows x 4 chunks of a V-operand
 //   transposing ds_read_b64 phase over distinct banks (no conflicts).
-template <int D, int KB>
+template <int D, int KB, int NW = 4>
 struct StageLayout {
   static_assert(KB == 32 || KB == 64, "tiles of 32 or 64 keys");
   static constexpr int kRow = D * 2;                  // bytes per row (K and V)
   static constexpr int kChunks = kRow / 16;           // 16-byte chunks per row
   static constexpr int kRowsPerInst = 64 / kChunks;   // rows one dwordx4 DMA instruction fills
-  static constexpr int kRowsPerWave = KB / 4;
+  static constexpr int kRowsPerWave = KB / NW;        // rows each of the NW waves loads
   static constexpr int kInstPerWave = kRowsPerWave / kRowsPerInst;
   static_assert(kInstPerWave >= 1, "a wave's rows fill whole DMA instructions");
 };
@@ -462,7 +462,6 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 // does not depend on the reference point.
 constexpr int kExtKB = 32;           // keys per tile
 constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
-constexpr int kExtWaves = 4;         // waves per workgroup, one per SIMD
 constexpr int kExtRows = 256;        // query rows per workgroup of the causal kernel: 4 waves x 64
 constexpr int kVerifyRows = 128;     // of the draft-tree verify kernel: 4 waves x 32
 constexpr int kExtAhead = kExtNS - 2;            // tiles in flight ahead of the math
@@ -525,6 +524,7 @@ __device__ __forceinline__ KFrags<D> ext_read_k(const char* kst, const ExtOffset
   return f;
 }
 
+// S^T of both row blocks (results in the MFMA's accumulation registers).
 // S^T of both row blocks (results in the MFMA's accumulation registers).
 template <int D, int RB>
 __device__ __forceinline__ void ext_qk(f32x16 (&sc)[RB], const KFrags<D>& kf, const bf16x8 (&qf)[RB][D / 16]) {
@@ -615,18 +615,18 @@ __device__ __forceinline__ void ext_pv(ExtState<D, RB>& es, const VFrags<D>& vf,
                                                                es.o[rb][mb], 0, 0, 0);
 }
 
-template <int D>
+template <int D, int NW>
 struct ExtStream {
   const char* kc;             // K pool at this KV head
   const char* vc;
   const int32_t* trow;        // index-table row
   uint32_t row_bytes;
-  uint32_t co[StageLayout<D, kExtKB>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
+  uint32_t co[StageLayout<D, kExtKB, NW>::kInstPerWave];   // this lane's swizzled chunk offset per DMA instruction
   int k1, ntiles, mask_from, wave_u, lane;
   int jrow;                   // this lane's row within a DMA instruction
   int hik;                    // 4 in the upper lane half: its score elements sit 4 keys later
   int lim[2];                 // last visible key position of this lane's row per block (-1: none)
-  float c;
+  float c;                    // sm_scale * log2(e)
   // draft-tree verify: keys at and past tree_base are visible to a row only where its
   // ancestor mask has their bit (key - tree_base); tree = false: plain causal
   bool tree;
@@ -635,10 +635,10 @@ struct ExtStream {
 };
 
 // LDS of the extend workgroup: the K/V stages and the slot-id ring.
-template <int D>
+template <int D, int NW>
 struct ExtShared {
   Stage<D, kExtKB> st[kExtNS];
-  int32_t ring[kExtRing][kExtWaves][kExtKB / kExtWaves];   // per tile and wave: its slot ids
+  int32_t ring[kExtRing][NW][kExtKB / NW];   // per tile and wave: its slot ids
 };
 
 // Global -> LDS loads issued through inline assembly.  The LDS address goes through M0,
@@ -666,9 +666,9 @@ __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {    // l
 
 // Slot ids of tile x into this wave's ring row: lane l < 8 loads the id of key 8*wave + l;
 // keys past k1 repeat the last slot.
-template <int D>
-__device__ __forceinline__ void ext_slot_dma(ExtShared<D>& sh, const ExtStream<D>& a, int x) {
-  constexpr int kPerWave = kExtKB / kExtWaves;
+template <int D, int NW>
+__device__ __forceinline__ void ext_slot_dma(ExtShared<D, NW>& sh, const ExtStream<D, NW>& a, int x) {
+  constexpr int kPerWave = kExtKB / NW;
   // lanes 0 .. kPerWave-1 load (one instruction per wave all the same, so the waits count)
   if (a.lane < kPerWave) {
     const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * kPerWave + a.lane, a.k1 - 1);
@@ -677,24 +677,24 @@ __device__ __forceinline__ void ext_slot_dma(ExtShared<D>& sh, const ExtStream<D
 }
 
 // This lane's slot id for each of its DMA instructions of tile x, from the ring.
-template <int D>
+template <int D, int NW>
 struct ExtRowSlots {
-  int s[StageLayout<D, kExtKB>::kInstPerWave];
+  int s[StageLayout<D, kExtKB, NW>::kInstPerWave];
 };
 
-template <int D>
-__device__ __forceinline__ ExtRowSlots<D> ext_read_slots(const ExtShared<D>& sh, const ExtStream<D>& a, int x) {
-  using L = StageLayout<D, kExtKB>;
-  ExtRowSlots<D> r;
+template <int D, int NW>
+__device__ __forceinline__ ExtRowSlots<D, NW> ext_read_slots(const ExtShared<D, NW>& sh, const ExtStream<D, NW>& a, int x) {
+  using L = StageLayout<D, kExtKB, NW>;
+  ExtRowSlots<D, NW> r;
 #pragma unroll
   for (int g = 0; g < L::kInstPerWave; ++g) r.s[g] = sh.ring[x % kExtRing][a.wave_u][g * L::kRowsPerInst + a.jrow];
   return r;
 }
 
 // Global -> LDS loads of this wave's K and V rows of one tile.
-template <int D>
-__device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStream<D>& a, const ExtRowSlots<D>& sl) {
-  using L = StageLayout<D, kExtKB>;
+template <int D, int NW>
+__device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStream<D, NW>& a, const ExtRowSlots<D, NW>& sl) {
+  using L = StageLayout<D, kExtKB, NW>;
 #pragma unroll
   for (int g = 0; g < L::kInstPerWave; ++g) {
     const uint64_t off = uint64_t(uint32_t(sl.s[g])) * a.row_bytes + a.co[g];
@@ -710,9 +710,9 @@ __device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStrea
 // a stage nobody reads), and loads complete in issue order: after tile t's loads come
 // those of the kExtAhead - 1 iterations since, so at most kAfter may stay outstanding.
 // Tiles issued before the loop wait for all.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void ext_wait(int t) {
-  constexpr int kAfter = (kExtAhead - 1) * (1 + 2 * StageLayout<D, kExtKB>::kInstPerWave);
+  constexpr int kAfter = (kExtAhead - 1) * (1 + 2 * StageLayout<D, kExtKB, NW>::kInstPerWave);
   static_assert(kAfter < 64, "vmcnt is 6 bits");
   if (t >= kExtAhead) wait_vmcnt_barrier<kAfter>();
   else wait_vmcnt_barrier<0>();
@@ -721,99 +721,110 @@ __device__ __forceinline__ void ext_wait(int t) {
 // Iteration t of the loop waits for tile t + 1 (its K is read ahead, at the end of
 // iteration t).  Tile t + 1 was issued by iteration t + 1 - kExtAhead (iteration 0 being
 // the tile-0 step), and kExtAhead - 2 iterations' loads came after it.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void ext_wait_next(int t) {
-  constexpr int kAfter = (kExtAhead - 2) * (1 + 2 * StageLayout<D, kExtKB>::kInstPerWave);
+  constexpr int kAfter = (kExtAhead - 2) * (1 + 2 * StageLayout<D, kExtKB, NW>::kInstPerWave);
   if (t + 1 >= kExtAhead) wait_vmcnt_barrier<kAfter>();
   else wait_vmcnt_barrier<0>();
 }
 
-// Scores of tile t to the next iteration's operand and, for MASK, -inf past this lane's last
-// visible key or the tile's last key.  The copy from the MFMA result registers is left to the
-// scheduler, which spreads it among the P.V MFMAs.
-template <int D, int RB, bool MASK>
-__device__ __forceinline__ void ext_take_scores(f32x16 (&dst)[RB], const f32x16 (&src)[RB], const ExtStream<D>& a, int t) {
+// -inf in the scores of tile t past this lane's last visible key or the tile's last key (and,
+// for the draft-tree verify, outside the row's ancestor mask).
+template <int D, int RB, int NW>
+__device__ __forceinline__ void ext_mask(f32x16 (&sc)[RB], const ExtStream<D, NW>& a, int t) {
+  const int key0 = t * kExtKB;
+  const int nk = min(kExtKB, a.k1 - key0);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) dst[rb] = src[rb];
-  if (MASK) {
-    const int key0 = t * kExtKB;
-    const int nk = min(kExtKB, a.k1 - key0);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int thr = min(a.lim[rb] - key0, nk - 1) - a.hik;
+    if (a.tree) {
+      // key k = key0 + hik + ext_key(j): causal bound as above, and past tree_base only
+      // the keys of the row's ancestor mask
+      const int rel0 = key0 + a.hik - a.tree_base;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int thr = min(a.lim[rb] - key0, nk - 1) - a.hik;
-      if (a.tree) {
-        // key k = key0 + hik + ext_key(j): causal bound as above, and past tree_base only
-        // the keys of the row's ancestor mask
-        const int rel0 = key0 + a.hik - a.tree_base;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rel = rel0 + ext_key(j);
-          const bool in_tree = rel < 0 || (rel < 64 && ((a.tm[rb] >> (rel & 63)) & 1));
-          if (ext_key(j) > thr || !in_tree) dst[rb][j] = -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (ext_key(j) > thr) dst[rb][j] = -INFINITY;
+      for (int j = 0; j < 16; ++j) {
+        const int rel = rel0 + ext_key(j);
+        const bool in_tree = rel < 0 || (rel < 64 && ((a.tm[rb] >> (rel & 63)) & 1));
+        if (ext_key(j) > thr || !in_tree) sc[rb][j] = -INFINITY;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (ext_key(j) > thr) sc[rb][j] = -INFINITY;
     }
   }
 }
 
-// Iterations [t_begin, t_end), t_begin >= 1.  On entry sprev holds S(t_begin - 1) in VGPRs,
-// kf K(t_begin) and vf V(t_begin - 1); on exit sprev holds S(t_end - 1).  Each iteration reads
-// the next K and V at its end, after its MFMAs are issued, so their LDS latency overlaps the
-// matrix work instead of delaying the next iteration's first MFMA.
-template <int D, int RB, bool MASK, bool TRACK>
-__device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
-                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D>& a, f32x16 (&sprev)[RB],
-                                          KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
+// Iteration t (t >= 1): on entry prev holds S(t-1) (relative to the reference, masked), kf
+// K(t) and vf V(t-1); on exit cur holds S(t), kf K(t+1) and vf V(t).  S(t) runs on the
+// matrix cores while the VALU turns S(t-1) into weights, then O += V(t-1)^T P(t-1).  The
+// next K and V are read at the end, after the MFMAs are issued, so their LDS latency
+// overlaps the matrix work instead of delaying the next iteration's first MFMA.
+template <int D, int RB, bool MASK, bool TRACK, int NW>
+__device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
+                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
+                                         const f32x16 (&prev)[RB], f32x16 (&cur)[RB], KFrags<D>& kf, VFrags<D>& vf,
+                                         int t) {
+  ext_wait_next<D, NW>(t);
+  const ExtRowSlots<D, NW> sl = ext_read_slots<D, NW>(sh, a, t + kExtAhead);
+  ext_slot_dma<D, NW>(sh, a, t + kExtSlotLead);
+  ext_kv_dma<D, NW>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
+  ext_qk<D, RB>(cur, kf, qf);
+  ExtWeights<RB> w;
+  ext_weights<D, RB, TRACK>(w, es, prev, a.c);
+  ext_pv<D, RB>(es, vf, w);
+  kf = ext_read_k<D>(sh.st[(t + 1) % kExtNS].k, off);
+  vf = ext_read_v<D>(sh.st[t % kExtNS].v, off);
+  if (MASK) ext_mask<D, RB, NW>(cur, a, t);
+  __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
+}
+
+// Iterations [t_begin, t_end), t_begin >= 1; sprev holds S(t_begin - 1) on entry and
+// S(t_end - 1) on exit.  (Unrolling by two so that two score buffers trade roles saves no
+// instruction: the scores come out of the MFMAs in accumulation registers and are moved to
+// VGPRs for the vector unit either way.)
+template <int D, int RB, bool MASK, bool TRACK, int NW>
+__device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
+                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
+                                          f32x16 (&sprev)[RB], KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
   for (int t = t_begin; t < t_end; ++t) {
-    ext_wait_next<D>(t);
-    const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, t + kExtAhead);
-    ext_slot_dma<D>(sh, a, t + kExtSlotLead);
-    ext_kv_dma<D>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
     f32x16 scur[RB];
-    ext_qk<D, RB>(scur, kf, qf);
-    ExtWeights<RB> w;
-    ext_weights<D, RB, TRACK>(w, es, sprev, a.c);
-    ext_pv<D, RB>(es, vf, w);
-    kf = ext_read_k<D>(sh.st[(t + 1) % kExtNS].k, off);
-    vf = ext_read_v<D>(sh.st[t % kExtNS].v, off);
-    ext_take_scores<D, RB, MASK>(sprev, scur, a, t);
-    __builtin_amdgcn_iglp_opt(0);   // interleave the MFMAs with the other work of the body
+    ext_iter<D, RB, MASK, TRACK, NW>(es, sh, off, qf, a, sprev, scur, kf, vf, t);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sprev[rb] = scur[rb];
   }
 }
 
 // One pass over keys [0, k1).  first_pass: each row's reference point is its maximum over
 // tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
-template <int D, int RB, bool TRACK>
-__device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D>& sh, const ExtOffsets<D>& off,
-                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D>& a, bool first_pass) {
+template <int D, int RB, bool TRACK, int NW>
+__device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
+                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool first_pass) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
   const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
   // prologue: slot ids of the first tiles, then their K/V
-  for (int x = 0; x < kExtSlotLead; ++x) ext_slot_dma<D>(sh, a, x);
+  for (int x = 0; x < kExtSlotLead; ++x) ext_slot_dma<D, NW>(sh, a, x);
   wait_vmcnt_barrier<0>();
-  for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D>(sh.st[x], a, ext_read_slots<D>(sh, a, x));
+  for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
   // tile 0: its scores only
-  ext_wait<D>(0);
-  ext_slot_dma<D>(sh, a, kExtSlotLead);
+  ext_wait<D, NW>(0);
+  ext_slot_dma<D, NW>(sh, a, kExtSlotLead);
   f32x16 sprev[RB];
   KFrags<D> kf;
   VFrags<D> vf;
   {
-    const ExtRowSlots<D> sl = ext_read_slots<D>(sh, a, kExtAhead);
+    const ExtRowSlots<D, NW> sl = ext_read_slots<D, NW>(sh, a, kExtAhead);
     kf = ext_read_k<D>(sh.st[0].k, off);
-    ext_kv_dma<D>(sh.st[kExtAhead % kExtNS], a, sl);
+    ext_kv_dma<D, NW>(sh.st[kExtAhead % kExtNS], a, sl);
     f32x16 scur[RB];
     ext_qk<D, RB>(scur, kf, qf);
     // every prologue tile has landed (the wait above counted to zero): tile 1's K and
     // tile 0's V for the first iteration
     kf = ext_read_k<D>(sh.st[1 % kExtNS].k, off);
     vf = ext_read_v<D>(sh.st[0].v, off);
-    if (t_mask == 0) ext_take_scores<D, RB, true>(sprev, scur, a, 0);
-    else ext_take_scores<D, RB, false>(sprev, scur, a, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sprev[rb] = scur[rb];
+    if (t_mask == 0) ext_mask<D, RB, NW>(sprev, a, 0);
   }
   if (first_pass) {
 #pragma unroll
@@ -824,8 +835,8 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D>& sh, 
     }
   }
   const int t_split = max(1, t_mask);
-  ext_iters<D, RB, false, TRACK>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
-  ext_iters<D, RB, true, TRACK>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
+  ext_iters<D, RB, false, TRACK, NW>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
+  ext_iters<D, RB, true, TRACK, NW>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
   // the last tile's weights and P.V (vf holds its V)
   ExtWeights<RB> w;
   ext_weights<D, RB, TRACK>(w, es, sprev, a.c);
@@ -885,19 +896,23 @@ __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool 
 }
 
 // TREE: draft-tree verify (tree_mask gives each row's ancestor mask); otherwise causal.
-template <int D, bool TREE>
-__global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
+// NW waves per workgroup: 4 (one per SIMD; 64 rows each in the causal kernel, 32 in the
+// verify kernel) or 8 (two per SIMD, 32 rows each).  The launchers use 4: on the mixed
+// batch the 8-wave form is 4% slower, with the same matrix-core busy cycles and the same
+// cycles of vector and matrix work overlapping, and more time waiting on dependencies.
+template <int D, bool TREE, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq,
     int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out, int uniform_n,
     const uint64_t* __restrict__ tree_mask) {
-  static_assert(kThreads == 64 * kExtWaves, "one wave per SIMD");
-  constexpr int RB = TREE ? 1 : 2;                // 32-row blocks per wave
-  constexpr int kRows = kExtWaves * 32 * RB;
+  static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+  constexpr int RB = (TREE || NW == 8) ? 1 : 2;   // 32-row blocks per wave
+  constexpr int kRows = NW * 32 * RB;
   static_assert(kRows == (TREE ? kVerifyRows : kExtRows), "rows per workgroup as the launchers assume");
-  __shared__ ExtShared<D> sh;
-  using L = StageLayout<D, kExtKB>;
+  __shared__ ExtShared<D, NW> sh;
+  using L = StageLayout<D, kExtKB, NW>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
   const int tpb = kRows / G;                      // tokens per tile
@@ -913,7 +928,7 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
   const int prefix = prefix_lens[b];
   const int qo = uniform_n > 0 ? b * uniform_n : qo_indptr[b];
   const int ntok = min(tpb, ext - t0);
-  ExtStream<D> a;
+  ExtStream<D, NW> a;
   a.tree = TREE;
   a.tree_base = prefix;
   bf16x8 qf[RB][D / 16];
@@ -957,13 +972,13 @@ __global__ void __launch_bounds__(kThreads, 1) extend_bf16_kernel(
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
   for (int pass = 0;; ++pass) {
-    ext_pass<D, RB, false>(es, sh, off, qf, a, pass == 0);
+    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0);
     const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
     if (pass == 1 || !__syncthreads_or(overflow)) break;
     // Some weight overflowed: find each row's true maximum, then recompute the rows
     // with it as the reference (the outputs above are overwritten).
     ext_reset<D, RB>(es);
-    ext_pass<D, RB, true>(es, sh, off, qf, a, true);
+    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true);
     float mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
@@ -1411,8 +1426,8 @@ int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_po
                        nullptr, prefix_lens, nullptr, n_qtiles, Hq, Hkv, sm_scale, nullptr,
                        static_cast<uint16_t*>(out), int(n), tree_mask);
   };
-  if (D == 128) args(extend_bf16_kernel<128, true>);
-  else args(extend_bf16_kernel<64, true>);
+  if (D == 128) args(extend_bf16_kernel<128, true, 4>);
+  else args(extend_bf16_kernel<64, true, 4>);
   return hip_check("rs_tree_verify_attention");
 }
 
@@ -1431,14 +1446,14 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     const int n_qtiles = (max_extend_len + tpb - 1) / tpb;
     const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
     if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");
-    auto args = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+    auto args = [&](auto kern, int threads) {
+      hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(threads), 0, s, static_cast<const uint16_t*>(q),
                          static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), req_to_token, ld,
                          qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale, order,
                          static_cast<uint16_t*>(out), 0, nullptr);
     };
-    if (D == 128) args(extend_bf16_kernel<128, false>);
-    else args(extend_bf16_kernel<64, false>);
+    if (D == 128) args(extend_bf16_kernel<128, false, 4>, 256);
+    else args(extend_bf16_kernel<64, false, 4>, 256);
     return hip_check("rs_extend_attention");
   }
   if (dtype == RS_DTYPE_F32) {
