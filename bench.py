@@ -13,9 +13,9 @@ contexts 1k-32k, GQA 64/8, d128, bf16, 4M-slot pool).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline] [--no-extra]
                     [--flush]
 
---flush overwrites a 1 GiB buffer before every timed step, so that a workload small enough
-to stay in L2 and the 256 MB MALL between steps is read from HBM each time; the step time
-is then the sum of the per-kernel event times (the flush itself is not counted).
+--flush reads a 1 GiB buffer before every timed step, so that a workload small enough to
+stay in L2 and the 256 MB MALL between steps is read from HBM each time; the step time is
+then the sum of the per-kernel event times (the flush itself is not counted).
 """
 from __future__ import annotations
 
@@ -253,12 +253,17 @@ def time_fn(fn, iters, warmup, flush=None):
 
 
 def make_flush(device="cuda", nbytes=1 << 30):
-    """Overwrites a 1 GiB buffer so L2 and the 256 MB MALL hold none of the next op's inputs."""
+    """Reads a 1 GiB buffer so that L2 and the 256 MB MALL hold none of the next op's inputs.
+
+    A read, not a fill: a fill leaves the caches full of dirty lines whose write-back to HBM
+    then runs during the timed op and competes with its reads (on the small decode workloads
+    that added 7-35 us to ops of 30-110 us)."""
     import torch
-    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    acc = torch.empty((), dtype=torch.float32, device=device)      # same dtype: one reduction kernel, no cast copy
 
     def flush():
-        buf.fill_(1)
+        torch.sum(buf, dim=0, out=acc)
     return flush
 
 
@@ -322,7 +327,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel runs of the other configs")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--flush", action="store_true",
-                    help="overwrite 1 GiB before every timed step (for workloads that fit in the caches)")
+                    help="read 1 GiB before every timed step (for workloads that fit in the caches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--host-tier", action="store_true",

@@ -277,10 +277,10 @@ int64_t rs_decode_plan_bytes(const rs_plan* p);
 int rs_decode_plan_upload(const rs_plan* p, void* dev, void* stream);
 /* Copy the device image into host memory (bytes >= rs_decode_plan_bytes), for inspection.
  * int32 words: header[16] = {magic, n_items, B, G, n_partials, off_items, off_item_req,
- * off_part_ptr, off_part_list, 0...}; items[n_items][8] = {k0, k1, rep_row, n_req,
- * req_off, part_base, 0, 0} (keys k0..k1-1 of table row rep_row, requests
- * item_req[req_off..+n_req), partials part_base..+n_req); item_req[]; part_ptr[B+1];
- * part_list[] (CSR: the partials of request b). */
+ * off_part_ptr, 0...}; items[n_items][8] = {k0, k1, rep_row, n_req, req_off, 0, 0, 0}
+ * (keys k0..k1-1 of table row rep_row for the requests of item_req[req_off..+n_req));
+ * item_req[][4] = {request b, partial index, partials of b, 0}; part_ptr[B+1]: request b's
+ * partials are part_ptr[b] .. part_ptr[b+1]-1, one per item that covers it. */
 int rs_decode_plan_read(const rs_plan* p, void* host, int64_t bytes);
 void rs_plan_destroy(rs_plan* p);
 

@@ -989,7 +989,10 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
 }
 
 // ------------------------------------------------------------------ decode (bf16)
-// Decode: 64-key tiles, two stages, up to two workgroups per CU.
+// Decode: kDecKB-key tiles through kDecNS LDS stages (kDecNS - 1 tiles in flight while one
+// is computed), up to two workgroups per CU.  Measured on the small decode batches and the
+// mixed batch: 32-key tiles through 4 or 5 stages (more bytes in flight, twice the waits and
+// barriers per key) are 4-10% slower than 64-key tiles through 2.
 constexpr int kDecKB = 64, kDecNS = 2;
 struct DecodeArgs {
   const uint16_t* q;
@@ -998,8 +1001,10 @@ struct DecodeArgs {
   const int32_t* req_to_token;
   int64_t ld;
   const int32_t* seq_lens;
-  const int32_t* plan;        // device image, or nullptr for the flat mode
-  int flat_nch;               // flat mode: chunks per request
+  const int32_t* items;       // plan: items [n_items][kItemWords]; nullptr: the flat mode
+  const int4* item_req;       // plan: {request, partial index, partials of the request, -}
+  const int32_t* part_ptr;    // plan: request b's partials are part_ptr[b] .. part_ptr[b+1]-1
+  int flat_nch;               // flat mode: chunks per request; request b's partials b*flat_nch + chunk
   int max_seq;                // flat mode: keys are read up to min(seq_lens[b], max_seq) only
   int Hq, Hkv;
   float sm_scale;
@@ -1010,29 +1015,10 @@ struct DecodeArgs {
   float* lse_out;             // [B][Hq] or nullptr
 };
 
-// Partials of request b: count and the i-th partial index.
-struct PartList {
-  const int32_t* list;
-  int base, n;
-  __device__ int at(int i) const { return list ? list[i] : base + i; }
-};
-
-// Partials of request b (plan: its CSR list; flat: its consecutive chunks).
-__device__ __forceinline__ PartList part_list(const DecodeArgs& a, int b) {
-  PartList pl;
-  if (a.plan) {
-    const int32_t* pp = a.plan + a.plan[7];
-    pl.list = a.plan + a.plan[8] + pp[b];
-    pl.base = 0;
-    pl.n = pp[b + 1] - pp[b];
-  } else {
-    pl.list = nullptr;
-    pl.base = b * a.flat_nch;
-    // a request longer than max_seq is cut to it, so its partials stay in its own range
-    pl.n = (min(a.seq_lens[b], a.max_seq) + rs::kFlatChunk - 1) / rs::kFlatChunk;
-  }
-  return pl;
-}
+// Flat mode: the keys of request b (a request longer than max_seq is cut to it, so that its
+// partials stay inside its own range) and its partial count.
+__device__ __forceinline__ int flat_len(const DecodeArgs& a, int b) { return min(a.seq_lens[b], a.max_seq); }
+__device__ __forceinline__ int flat_parts(int len) { return (len + rs::kFlatChunk - 1) / rs::kFlatChunk; }
 
 // One work item per (item, KV head): its key chunk for all query rows of its row tile.
 // A request covered by this single item gets its final output here; otherwise the
@@ -1044,22 +1030,23 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   const int G = a.Hq / a.Hkv;
   const int kvh = blockIdx.x % a.Hkv;
   const int item = blockIdx.x / a.Hkv;
-  int k0, k1, rep, nreq, req_off = 0, part_base;
-  if (a.plan) {
-    const int32_t* it = a.plan + a.plan[5] + item * rs::kItemWords;
-    k0 = it[0]; k1 = it[1]; rep = it[2]; nreq = it[3]; req_off = it[4]; part_base = it[5];
-  } else {
-    const int b = item / a.flat_nch, ch = item % a.flat_nch;
-    k0 = ch * rs::kFlatChunk;
-    k1 = min(k0 + rs::kFlatChunk, min(a.seq_lens[b], a.max_seq));
-    if (k0 >= k1) return;
-    rep = b; nreq = 1; part_base = item;
-  }
-  const int32_t* item_req = a.plan ? a.plan + a.plan[6] + req_off : nullptr;
   const int row = wave * 32 + (lane & 31);
   const int j = row / G, g = row % G;
+  int k0, k1, rep, nreq, b, pidx, nparts;
+  if (a.items) {
+    const int32_t* it = a.items + item * rs::kItemWords;
+    k0 = it[0]; k1 = it[1]; rep = it[2]; nreq = it[3];
+    const int4 e = j < nreq ? a.item_req[it[4] + j] : make_int4(rep, 0, 0, 0);
+    b = e.x; pidx = e.y; nparts = e.z;
+  } else {
+    rep = b = item / a.flat_nch;
+    const int ch = item % a.flat_nch, len = flat_len(a, b);
+    k0 = ch * rs::kFlatChunk;
+    k1 = min(k0 + rs::kFlatChunk, len);
+    if (k0 >= k1) return;
+    nreq = 1; pidx = item; nparts = flat_parts(len);
+  }
   const bool valid = j < nreq;
-  const int b = valid ? (item_req ? item_req[j] : rep) : 0;
   const int64_t qrow_idx = int64_t(b) * a.Hq + kvh * G + g;
   bf16x8 qf[D / 16];
   load_q<D>(qf, a.q + qrow_idx * D, valid, lane);
@@ -1074,7 +1061,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse = ws.m * a.sm_scale + __logf(l);
   const int hi = lane >> 5;
-  if (part_list(a, b).n == 1) {          // this item covers the request: final output
+  if (nparts == 1) {                     // this item covers the request: final output
     uint16_t* orow = a.out + qrow_idx * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -1089,8 +1076,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
     if (hi == 0 && a.lse_out) a.lse_out[qrow_idx] = lse;
     return;
   }
-  const int64_t p = part_base + j;
-  float* orow = a.o_part + ((int64_t(kvh) * a.n_partials + p) * G + g) * D;
+  float* orow = a.o_part + ((int64_t(kvh) * a.n_partials + pidx) * G + g) * D;
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -1100,116 +1086,75 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
           make_float4(ws.o[mb][4 * q4 + 0] * inv, ws.o[mb][4 * q4 + 1] * inv, ws.o[mb][4 * q4 + 2] * inv,
                       ws.o[mb][4 * q4 + 3] * inv);
     }
-  if (hi == 0) a.lse_part[(int64_t(kvh) * a.n_partials + p) * G + g] = lse;
+  if (hi == 0) a.lse_part[(int64_t(kvh) * a.n_partials + pidx) * G + g] = lse;
 }
 
 // Log-sum-exp merge of each (request, KV head)'s partials:
 //   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
-// Per group of up to 16 query heads: each wave reduces the max and the sum of its heads'
-// lse over the partials (64 partials per step, lane-parallel); the weights of a batch of
-// kMergeBatch partials go to LDS; then every thread accumulates its output elements over
-// the batch, four partials per step so their loads are in flight together.
-constexpr int kMergeBatch = 64;
-constexpr int kMergeHeads = 16;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// A request's partials sit consecutively in the workspace, so the workgroup finds them from
+// two numbers.  Each thread owns four consecutive output elements (of one query head) and
+// loads the lse and the four values of a batch of kMergeBatch partials at once, so that the
+// loads of a batch are in flight together; a running maximum keeps the sums finite across
+// batches.
+constexpr int kMergeBatch = 16;
 
 template <int D>
 __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
-  __shared__ float s_w[kMergeHeads * kMergeBatch];   // weights [g][i] of the current batch
-  __shared__ int s_p[kMergeBatch];
-  __shared__ float s_m[kMergeHeads], s_sum[kMergeHeads];
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
-  const PartList pl = part_list(a, b);
-  if (pl.n <= 1) return;
+  int base, n;
+  if (a.part_ptr) {
+    base = a.part_ptr[b];
+    n = a.part_ptr[b + 1] - base;
+  } else {
+    base = b * a.flat_nch;
+    n = flat_parts(flat_len(a, b));
+  }
+  if (n <= 1) return;
   const int G = a.Hq / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* op = a.o_part + int64_t(kvh) * a.n_partials * G * D;
-  const float* lp = a.lse_part + int64_t(kvh) * a.n_partials * G;
-  for (int g0 = 0; g0 < G; g0 += kMergeHeads) {
-    const int ng = min(kMergeHeads, G - g0);
-    // pass 1: max and sum of exp over all partials, one head per wave at a time
-    for (int g = wave; g < ng; g += kThreads / 64) {
-      float m = -INFINITY, sum = 0.f;
-      for (int i0 = 0; i0 < pl.n; i0 += 64) {
-        const int i = i0 + lane;
-        const float v = i < pl.n ? lp[int64_t(pl.at(i)) * G + g0 + g] : -INFINITY;
-        const float m_new = fmaxf(m, wave_max(v));
-        if (m_new != -INFINITY) {
-          sum = sum * __expf(m - m_new) + wave_sum(__expf(v - m_new));
-          m = m_new;
+  const float* op = a.o_part + (int64_t(kvh) * a.n_partials + base) * G * D;   // [n][G][D]
+  const float* lp = a.lse_part + (int64_t(kvh) * a.n_partials + base) * G;     // [n][G]
+  for (int e0 = 4 * int(threadIdx.x); e0 < G * D; e0 += 4 * kThreads) {
+    const int g = e0 / D;
+    float m = -INFINITY, sum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+      float l[kMergeBatch];
+      float4 o[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (i0 + i < n) {
+          l[i] = lp[int64_t(i0 + i) * G + g];
+          o[i] = *reinterpret_cast<const float4*>(op + int64_t(i0 + i) * G * D + e0);
+        } else {
+          l[i] = -INFINITY;
+          o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
-      if (lane == 0) {
-        s_m[g] = m;
-        s_sum[g] = sum;
+      float mb = m;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) mb = fmaxf(mb, l[i]);
+      // mb is finite: every partial covers at least one key
+      const float r = __expf(m - mb);    // 0 before the first batch
+      sum *= r;
+      acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const float w = __expf(l[i] - mb);
+        sum += w;
+        acc.x = fmaf(w, o[i].x, acc.x);
+        acc.y = fmaf(w, o[i].y, acc.y);
+        acc.z = fmaf(w, o[i].z, acc.z);
+        acc.w = fmaf(w, o[i].w, acc.w);
       }
+      m = mb;
     }
-    __syncthreads();
-    constexpr int kPer = kMergeHeads * D / kThreads;   // element slots per thread
-    const int n_el = ng * D;
-    float acc[kPer];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-    for (int i0 = 0; i0 < pl.n; i0 += kMergeBatch) {
-      const int nb = min(kMergeBatch, pl.n - i0);
-      if (tid < nb) s_p[tid] = pl.at(i0 + tid);
-      __syncthreads();
-      for (int x = tid; x < nb * ng; x += kThreads) {
-        const int i = x / ng, g = x % ng;
-        s_w[g * kMergeBatch + i] = __expf(lp[int64_t(s_p[i]) * G + g0 + g] - s_m[g]) / s_sum[g];
-      }
-      __syncthreads();
-      int i = 0;
-      for (; i + 4 <= nb; i += 4) {
-        const float* src0 = op + (int64_t(s_p[i + 0]) * G + g0) * D;
-        const float* src1 = op + (int64_t(s_p[i + 1]) * G + g0) * D;
-        const float* src2 = op + (int64_t(s_p[i + 2]) * G + g0) * D;
-        const float* src3 = op + (int64_t(s_p[i + 3]) * G + g0) * D;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int idx = tid + e * kThreads;            // (g, d) flattened
-          if (idx < n_el) {
-            const float* w = s_w + (idx / D) * kMergeBatch + i;
-            const float x0 = src0[idx], x1 = src1[idx], x2 = src2[idx], x3 = src3[idx];
-            acc[e] = fmaf(w[0], x0, acc[e]);
-            acc[e] = fmaf(w[1], x1, acc[e]);
-            acc[e] = fmaf(w[2], x2, acc[e]);
-            acc[e] = fmaf(w[3], x3, acc[e]);
-          }
-        }
-      }
-      for (; i < nb; ++i) {
-        const float* src = op + (int64_t(s_p[i]) * G + g0) * D;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int idx = tid + e * kThreads;
-          if (idx < n_el) acc[e] = fmaf(s_w[(idx / D) * kMergeBatch + i], src[idx], acc[e]);
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int idx = tid + e * kThreads;
-      if (idx < n_el) {
-        const int g = idx / D, d = idx % D;
-        const int64_t orow = int64_t(b) * a.Hq + kvh * G + g0 + g;
-        a.out[orow * D + d] = f2bf(acc[e]);
-        if (d == 0 && a.lse_out) a.lse_out[orow] = s_m[g] + __logf(s_sum[g]);
-      }
-    }
-    __syncthreads();
+    const float inv = 1.f / sum;
+    const int64_t orow = int64_t(b) * a.Hq + kvh * G + g;
+    uint2 u;
+    u.x = pack_bf16(acc.x * inv, acc.y * inv);
+    u.y = pack_bf16(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(a.out + orow * D + e0 % D) = u;
+    if (a.lse_out && e0 % D == 0) a.lse_out[orow] = m + __logf(sum);
   }
 }
 
@@ -1492,6 +1437,8 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
   if (dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: dtype");
   if ((plan == nullptr) != (plan_dev == nullptr))
     return rs::fail(RS_E_INVAL, "rs_decode_attention: pass both the plan and its device image, or neither");
+  if (reinterpret_cast<uintptr_t>(plan_dev) & 15)
+    return rs::fail(RS_E_INVAL, "rs_decode_attention: the plan image must be 16-byte aligned");
   int64_t P, items;
   int flat_nch = 0;
   if (plan) {
@@ -1516,7 +1463,16 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
   a.req_to_token = req_to_token;
   a.ld = ld;
   a.seq_lens = seq_lens;
-  a.plan = static_cast<const int32_t*>(plan_dev);
+  a.items = nullptr;
+  a.item_req = nullptr;
+  a.part_ptr = nullptr;
+  if (plan) {
+    const rs::PlanOffsets po = rs::plan_offsets(plan);
+    const int32_t* img = static_cast<const int32_t*>(plan_dev);
+    a.items = img + po.items;
+    a.item_req = reinterpret_cast<const int4*>(img + po.item_req);
+    a.part_ptr = img + po.part_ptr;
+  }
   a.flat_nch = flat_nch;
   a.max_seq = max_seq_len;
   a.Hq = Hq;

@@ -56,6 +56,8 @@ WsLayout ws_layout(int64_t n_partials, int32_t B, int32_t Hq, int32_t Hkv, int32
 
 const rs_plan_info_t* plan_info(const rs_plan* p) { return &p->info; }
 
+PlanOffsets plan_offsets(const rs_plan* p) { return PlanOffsets{p->image[5], p->image[6], p->image[7]}; }
+
 }  // namespace rs
 
 extern "C" {
@@ -131,32 +133,40 @@ int rs_decode_plan_build(const rs_tree* t, const int64_t* nodes, const int32_t* 
     int64_t chunk = (work + target - 1) / target;
     chunk = std::min<int64_t>(std::max<int64_t>((chunk + 63) / 64 * 64, rs::kMinChunk), rs::kMaxChunk);
 
-    // 4. items
+    // 4. items; item_req entries {request, partial index, partials of the request, 0}.  A
+    // request's partials are numbered consecutively (part_ptr[b] .. part_ptr[b+1]-1), so the
+    // merge finds them without a list.
     std::vector<int32_t> items, item_req;
-    std::vector<std::vector<int32_t>> parts(B);
-    int64_t P = 0;
+    std::vector<int32_t> n_parts(B, 0);
     int32_t n_items = 0;
     for (auto& s : segs) {
       int32_t len = s.end - s.start;
       int32_t nch = int32_t((len + chunk - 1) / chunk);
-      int32_t per = ((len + nch - 1) / nch + 63) / 64 * 64;          // even chunks, multiple of 64
+      int32_t per = ((len + nch - 1) / nch + rs::kChunkAlign - 1) / rs::kChunkAlign * rs::kChunkAlign;
       int32_t nreq = int32_t(s.reqs.size());
       for (int32_t k0 = s.start; k0 < s.end; k0 += per) {
         int32_t k1 = std::min(s.end, k0 + per);
         for (int32_t r0 = 0; r0 < nreq; r0 += rpt) {
           int32_t nr = std::min(rpt, nreq - r0);
-          int32_t req_off = int32_t(item_req.size());
+          int32_t req_off = int32_t(item_req.size() / rs::kItemReqWords);
           for (int32_t j = 0; j < nr; ++j) {
             int32_t b = s.reqs[r0 + j];
-            item_req.push_back(b);
-            parts[b].push_back(int32_t(P + j));
+            int32_t e[rs::kItemReqWords] = {b, n_parts[b]++, 0, 0};   // local index for now
+            item_req.insert(item_req.end(), e, e + rs::kItemReqWords);
           }
-          int32_t it[rs::kItemWords] = {k0, k1, s.rep, nr, req_off, int32_t(P), 0, 0};
+          int32_t it[rs::kItemWords] = {k0, k1, s.rep, nr, req_off, 0, 0, 0};
           items.insert(items.end(), it, it + rs::kItemWords);
-          P += nr;
           ++n_items;
         }
       }
+    }
+    std::vector<int32_t> part_ptr(B + 1, 0);
+    for (int32_t b = 0; b < B; ++b) part_ptr[b + 1] = part_ptr[b] + n_parts[b];
+    const int64_t P = part_ptr[B];
+    for (size_t e = 0; e < item_req.size(); e += rs::kItemReqWords) {
+      const int32_t b = item_req[e];
+      item_req[e + 1] += part_ptr[b];
+      item_req[e + 2] = n_parts[b];
     }
     if (P >= (int64_t(1) << 31) / (int64_t(G) * D * Hkv))
       return rs::fail(RS_E_UNSUPPORTED, "rs_decode_plan_build: batch too large for one plan");
@@ -186,17 +196,10 @@ int rs_decode_plan_build(const rs_tree* t, const int64_t* nodes, const int32_t* 
     img[4] = int32_t(P);
     img[5] = int32_t(img.size());
     img.insert(img.end(), items.begin(), items.end());
-    img[6] = int32_t(img.size());
+    img[6] = int32_t(img.size());                    // 16-byte aligned: header and items are whole vectors
     img.insert(img.end(), item_req.begin(), item_req.end());
     img[7] = int32_t(img.size());
-    int32_t acc = 0;
-    img.push_back(0);
-    for (int32_t b = 0; b < B; ++b) {
-      acc += int32_t(parts[b].size());
-      img.push_back(acc);
-    }
-    img[8] = int32_t(img.size());
-    for (int32_t b = 0; b < B; ++b) img.insert(img.end(), parts[b].begin(), parts[b].end());
+    img.insert(img.end(), part_ptr.begin(), part_ptr.end());
     while (img.size() % 4) img.push_back(0);
 
     rs_plan_info_t& in = p->info;

@@ -25,10 +25,9 @@ def _admit(wl):
 def _decode_view(img):
     n_items, B, G, P = img[1], img[2], img[3], img[4]
     items = img[img[5]:img[5] + 8 * n_items].reshape(n_items, 8)
-    item_req = img[img[6]:img[7]]
+    item_req = img[img[6]:img[7]].reshape(-1, 4)
     part_ptr = img[img[7]:img[7] + B + 1]
-    part_list = img[img[8]:img[8] + P]
-    return items, item_req, part_ptr, part_list
+    return items, item_req, part_ptr
 
 
 def check_plan(wl, t, table, nodes, reqs, base_row):
@@ -38,24 +37,26 @@ def check_plan(wl, t, table, nodes, reqs, base_row):
     p = rs.Plan(t, nodes[base_row:base_row + len(reqs)], cached, seq, Hq, Hkv, D)
     img = p.image()
     assert img[0] == 0x52535031 and img[2] == len(reqs) and img[3] == Hq // Hkv
-    items, item_req, part_ptr, part_list = _decode_view(img)
+    items, item_req, part_ptr = _decode_view(img)
     sub = table[base_row:base_row + len(reqs)]
     cover = [np.zeros(s, np.int32) for s in seq]
     owner = {}
-    for it_idx, (k0, k1, rep, nreq, off, pbase, _a, _b) in enumerate(items):
+    for it_idx, (k0, k1, rep, nreq, off, _a, _b, _c) in enumerate(items):
         assert 0 <= k0 < k1 and 1 <= nreq and nreq * (Hq // Hkv) <= 128
         for j in range(nreq):
-            b = item_req[off + j]
+            b, pidx, nparts, _z = item_req[off + j]
             assert k1 <= seq[b]
             cover[b][k0:k1] += 1
             # the representative row's slots are this request's slots
             np.testing.assert_array_equal(sub[rep, k0:k1], sub[b, k0:k1])
-            owner[pbase + j] = b
+            # a request's partials are numbered consecutively from part_ptr[b], each once
+            assert part_ptr[b] <= pidx < part_ptr[b + 1] and nparts == part_ptr[b + 1] - part_ptr[b]
+            assert pidx not in owner
+            owner[pidx] = b
     for b in range(len(reqs)):
         assert (cover[b] == 1).all(), b
-        for pi in part_list[part_ptr[b]:part_ptr[b + 1]]:
-            assert owner[pi] == b
-    assert part_ptr[-1] == img[4] == len(owner)
+    assert part_ptr[0] == 0 and part_ptr[-1] == img[4] == len(owner)
+    assert img[6] % 4 == 0                      # item_req is read as 16-byte vectors
     uniq = set()
     for b in range(len(reqs)):
         uniq.update(sub[b, :seq[b]].tolist())
