@@ -1091,6 +1091,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a) 
 
 // Log-sum-exp merge of each (request, KV head)'s partials:
 //   lse = log sum_i exp(lse_i),  o = sum_i exp(lse_i - lse) o_i.
+// A second launch: merging inside the decode kernel (the workgroup that writes a request's
+// last partial merges it, partials exchanged through agent-scope atomic stores and loads)
+// measured 1.6-5x slower, because the last workgroups to finish are the long shared-segment
+// items, which then merge dozens of requests one after another.
 // A request's partials sit consecutively in the workspace, so the workgroup finds them from
 // two numbers.  Each thread owns four consecutive output elements (of one query head) and
 // loads the lse and the four values of a batch of kMergeBatch partials at once, so that the

@@ -388,6 +388,31 @@ def test_decode_plan_repeat_bit_identical(torch_rs):
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
+def test_decode_consecutive_launches_merge_their_own_partials(torch_rs):
+    """Partials live in the workspace across launches: each launch, with other queries
+    (scaled by powers of two, exact in bf16), must merge only its own partials, in plan mode
+    and in flat mode."""
+    torch, rs = torch_rs
+    _say("config 4 decode: three launches with different queries, plan and flat")
+    b = _bench()
+    st = b.setup(4)
+    b.run_store(st)
+    q0 = st.q_dec.clone()
+    kv = [st.vals.kv_rows(r.tokens, 0, r.seq_len) for r in st.dec]
+    qs = [st.vals.q_rows(r.tokens, r.seq_len - 1, r.seq_len) for r in st.dec]
+    for scale in (1.0, -0.5, 2.0, 1.0):
+        st.q_dec.copy_(q0 * scale)
+        for flat in (False, True):
+            b.run_decode(st, flat=flat)
+            torch.cuda.synchronize()
+            got, gl = st.out_dec.float().cpu().numpy(), st.lse_dec.cpu().numpy()
+            for i, r in enumerate(st.dec):
+                o, l = oracle.attend(qs[i] * scale, kv[i][0], kv[i][1], [r.seq_len - 1], st.wl.sm_scale)
+                mx, rel = bf16_request_errors(got[i], o[0])
+                assert mx <= BF16_MAX_ABS and rel <= BF16_REL_RMS, (scale, flat, i, mx, rel)
+                assert np.abs(gl[i] - l[0]).max() <= LSE_MAX_ABS, (scale, flat, i)
+
+
 def test_config3_multistep_agent_extend(torch_rs):
     torch, rs = torch_rs
     _say("config 3 extend bf16 (64 users)")
