@@ -398,6 +398,23 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool,
                         float sm_scale, int32_t dtype, const rs_plan* plan, const void* plan_dev,
                         void* ws, int64_t ws_bytes, void* out, float* lse_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): rs_decode_attention with the workspace
+ * taken from a static device array of the library (128 MiB per GPU, held from the library's
+ * first use on that GPU until the process ends; its device address is looked up once per
+ * device with hipGetSymbolAddress).  Same arguments and results as rs_decode_attention
+ * without ws / ws_bytes; the caller still passes every input and output.  A batch whose
+ * workspace (rs_decode_workspace_bytes) exceeds 128 MiB is refused with RS_E_UNSUPPORTED
+ * before anything runs.  No memory is allocated or freed, and nothing in the array needs
+ * clearing: every partial is written before it is read within a call.  All calls on one
+ * GPU share the array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller. */
+int rs_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* req_to_token, int64_t ld, const int32_t* seq_lens,
+                                int32_t B, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D,
+                                float sm_scale, int32_t dtype, const rs_plan* plan,
+                                const void* plan_dev, void* out, float* lse_out, void* stream);
+
 /* Merge two attention states over disjoint key sets (the combine step above), rows x D:
  * o_a, o_b, o: device [rows][D] of dtype; lse_*: device float [rows]. */
 int rs_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,

@@ -15,6 +15,7 @@ from ._lib import (Tree, Plan, RsError, NoSpaceError, StaleError, DTYPE_F32, DTY
                    decode_workspace_bytes, extend_order, draft_tree_build, LIB_PATH)
 
 __all__ = ["Tree", "Plan", "RsError", "NoSpaceError", "StaleError", "store_kv", "extend_attention",
+           "decode_attention_noalloc",
            "decode_attention", "merge_states", "DecodeWorkspace", "draft_tree_build", "tree_verify_attention",
            "move_kv", "copy_kv", "host_pool", "LIB_PATH"]
 
@@ -155,6 +156,21 @@ def decode_attention(q, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_
                           plan_dev.data_ptr() if plan_dev is not None else None,
                           workspace.buf.data_ptr(), workspace.nbytes, _dev(out, "out", k_pool.dtype),
                           _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(stream))
+    return out
+
+
+def decode_attention_noalloc(q, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, out, plan=None,
+                             plan_dev=None, lse=None, stream=None):
+    """decode_attention with the library's static workspace: allocates nothing (out is required)."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    ld = req_to_token.shape[1]
+    _lib.decode_attention_noalloc(_dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                                  _dev(v_pool, "v_pool", k_pool.dtype), _dev(req_to_token, "req_to_token", torch.int32),
+                                  ld, _dev(seq_lens, "seq_lens", torch.int32), B, max_seq_len, Hq, Hkv, D, sm_scale,
+                                  _dtype(k_pool), plan, plan_dev.data_ptr() if plan_dev is not None else None,
+                                  _dev(out, "out", k_pool.dtype),
+                                  _dev(lse, "lse", torch.float32) if lse is not None else None, _stream(stream))
     return out
 
 

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librs.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("librs.so is not built: run `python -m radix_tree_prefix_amd.build` "
+    raise ImportError("librs.so is not built: run `python radix_tree_prefix_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 lib = C.CDLL(LIB_PATH)
@@ -117,6 +117,8 @@ _SIGS = {
     "rs_evict_host": (C.c_int64, [_P, C.c_int64]),
     "rs_decode_attention": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.c_float, C.c_int32, _P, _P, _P, C.c_int64, _P, _P, _P]),
+    "rs_decode_attention_noalloc": (C.c_int, [_P, _P, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32,
+                                              C.c_int32, C.c_int32, C.c_float, C.c_int32, _P, _P, _P, _P, _P]),
     "rs_merge_states": (C.c_int, [_P, _P, _P, _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -401,6 +403,14 @@ def decode_attention(q, k_pool, v_pool, req_to_token, ld, seq_lens, B, max_seq_l
                                    int(Hq), int(Hkv), int(D), float(sm_scale), int(dtype),
                                    plan.handle if plan is not None else None, plan_dev, ws, int(ws_bytes), out,
                                    lse_out, C.c_void_p(stream)))
+
+
+def decode_attention_noalloc(q, k_pool, v_pool, req_to_token, ld, seq_lens, B, max_seq_len, Hq, Hkv, D, sm_scale,
+                             dtype, plan, plan_dev, out, lse_out, stream=0):
+    _check(lib.rs_decode_attention_noalloc(q, k_pool, v_pool, req_to_token, int(ld), seq_lens, int(B),
+                                           int(max_seq_len), int(Hq), int(Hkv), int(D), float(sm_scale), int(dtype),
+                                           plan.handle if plan is not None else None, plan_dev, out, lse_out,
+                                           C.c_void_p(stream)))
 
 
 def merge_states(o_a, lse_a, o_b, lse_b, rows, D, dtype, o, lse, stream=0):

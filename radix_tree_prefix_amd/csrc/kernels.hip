@@ -27,6 +27,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -1316,6 +1317,43 @@ bool dims_ok(int32_t Hq, int32_t Hkv, int32_t D) {
   return Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq / Hkv <= rs::kMaxRowsPerItem && (D == 64 || D == 128);
 }
 
+// ------------------------------------------------------------------ allocation-free decode scratch
+// The workspace of rs_decode_attention_noalloc: a file-scope device array, one per GPU the
+// library runs on, held until the process ends.  Host code never uses the array's name as a
+// device address (on the host it is only a stand-in for the symbol): the address is looked
+// up once per device with hipGetSymbolAddress, with that device current, and kept.
+constexpr int64_t kNoallocScratchBytes = int64_t(128) << 20;
+__device__ __align__(256) char g_noalloc_scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr and rs_last_error set on failure).
+void* noalloc_scratch() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    rs::fail(RS_E_HIP, std::string("rs_decode_attention_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention_noalloc: device index beyond " + std::to_string(kMaxDevices));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch));
+    if (e != hipSuccess || !p) {
+      rs::fail(RS_E_HIP, std::string("rs_decode_attention_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI (device ops)
@@ -1497,6 +1535,25 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
     hipLaunchKernelGGL(decode_merge_kernel<64>, g_merge, dim3(kThreads), 0, s, a);
   }
   return hip_check("rs_decode_attention");
+}
+
+int rs_decode_attention_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* req_to_token,
+                                int64_t ld, const int32_t* seq_lens, int32_t B, int32_t max_seq_len, int32_t Hq,
+                                int32_t Hkv, int32_t D, float sm_scale, int32_t dtype, const rs_plan* plan,
+                                const void* plan_dev, void* out, float* lse_out, void* stream) {
+  int64_t need = 0;
+  if (dtype == RS_DTYPE_BF16 && B > 0) {
+    need = rs_decode_workspace_bytes(plan, B, max_seq_len, Hq, Hkv, D);
+    if (need < 0) return int(need);
+    if (need > kNoallocScratchBytes)
+      return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention_noalloc: the batch needs a " + std::to_string(need) +
+                                            "-byte workspace, the static scratch holds " +
+                                            std::to_string(kNoallocScratchBytes));
+  }
+  void* ws = need > 0 ? noalloc_scratch() : nullptr;
+  if (need > 0 && !ws) return RS_E_HIP;
+  return rs_decode_attention(q, k_pool, v_pool, req_to_token, ld, seq_lens, B, max_seq_len, Hq, Hkv, D, sm_scale,
+                             dtype, plan, plan_dev, ws, need, out, lse_out, stream);
 }
 
 int rs_decode_workspace_init(void* ws, int64_t ws_bytes, void* stream) {
