@@ -901,7 +901,7 @@ __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool 
 // verify kernel) or 8 (two per SIMD, 32 rows each).  The launchers use 4: on the mixed
 // batch the 8-wave form is 4% slower, with the same matrix-core busy cycles and the same
 // cycles of vector and matrix work overlapping, and more time waiting on dependencies.
-template <int D, bool TREE, int NW>
+template <int D, bool TREE, int NW, int RB>
 __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
@@ -909,9 +909,8 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
     int Hkv, float sm_scale, const int32_t* __restrict__ order, uint16_t* __restrict__ out, int uniform_n,
     const uint64_t* __restrict__ tree_mask) {
   static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
-  constexpr int RB = (TREE || NW == 8) ? 1 : 2;   // 32-row blocks per wave
-  constexpr int kRows = NW * 32 * RB;
-  static_assert(kRows == (TREE ? kVerifyRows : kExtRows), "rows per workgroup as the launchers assume");
+  static_assert(RB == 1 || RB == 2, "32-row blocks per wave");
+  constexpr int kRows = NW * 32 * RB;                // rows per workgroup (the launcher sizes the grid by it)
   __shared__ ExtShared<D, NW> sh;
   using L = StageLayout<D, kExtKB, NW>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1413,8 +1412,8 @@ int rs_tree_verify_attention(const void* q, const void* k_pool, const void* v_po
                        nullptr, prefix_lens, nullptr, n_qtiles, Hq, Hkv, sm_scale, nullptr,
                        static_cast<uint16_t*>(out), int(n), tree_mask);
   };
-  if (D == 128) args(extend_bf16_kernel<128, true, 4>);
-  else args(extend_bf16_kernel<64, true, 4>);
+  if (D == 128) args(extend_bf16_kernel<128, true, 4, 1>);
+  else args(extend_bf16_kernel<64, true, 4, 1>);
   return hip_check("rs_tree_verify_attention");
 }
 
@@ -1429,7 +1428,12 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     return rs::fail(RS_E_INVAL, "rs_extend_attention: null pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == RS_DTYPE_BF16) {
-    const int G = Hq / Hkv, tpb = kExtRows / G;
+    // 256 query rows per workgroup.  With 4 query heads per KV head and 200-token extends the
+    // last q-tile is 87% empty, yet 128-row workgroups (one 32-row block per wave, as the
+    // verify kernel) measured 5% slower on that batch: they halve the MFMAs per tile, not
+    // the per-tile overhead.
+    const int G = Hq / Hkv;
+    const int tpb = kExtRows / G;
     const int n_qtiles = (max_extend_len + tpb - 1) / tpb;
     const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
     if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");
@@ -1439,8 +1443,8 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
                          qo_indptr, prefix_lens, extend_lens, n_qtiles, Hq, Hkv, sm_scale, order,
                          static_cast<uint16_t*>(out), 0, nullptr);
     };
-    if (D == 128) args(extend_bf16_kernel<128, false, 4>, 256);
-    else args(extend_bf16_kernel<64, false, 4>, 256);
+    if (D == 128) args(extend_bf16_kernel<128, false, 4, 2>, 256);
+    else args(extend_bf16_kernel<64, false, 4, 2>, 256);
     return hip_check("rs_extend_attention");
   }
   if (dtype == RS_DTYPE_F32) {
