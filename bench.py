@@ -49,8 +49,12 @@ def _chunks(n, size):
         yield i, min(n, i + size)
 
 
-def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
-    """Admit a workload through librs and make its batch resident on the GPU."""
+def setup(cfg=5, device="cuda", build_plan=True, schedule=None, **wl_kw):
+    """Admit a workload through librs and make its batch resident on the GPU.
+
+    schedule=None admits the batch in request order; "lpm" / "dfs-weight" / "fcfs" admits it
+    in the order rs_schedule gives its cached parts as a waiting queue on the tree the history
+    left (st.admit_order); each request keeps its own table row either way."""
     import torch
     import radix_tree_prefix_amd as rs
 
@@ -86,14 +90,18 @@ def setup(cfg=5, device="cuda", build_plan=True, **wl_kw):
     st.sched_dfs_s = time.perf_counter() - t0
     st.sched_n = len(queue)
 
-    # batch: admit every request in order, its slots straight into its table row
-    # table rows padded to 64 bytes, as an engine allocates its request-to-token pool
+    # batch: admit every request (in the scheduler's order if asked), its slots straight into
+    # its table row; table rows padded to 64 bytes, as an engine allocates its request-to-token pool
+    order = list(range(wl.B))
+    if schedule is not None:
+        order = [int(i) for i in tree.schedule([r.tokens[:r.cached] for r in wl.requests], schedule)[0]]
+    st.admit_order = order
     ld = -(-max(r.seq_len for r in wl.requests) // 16) * 16
     table = np.full((wl.B, ld), -1, np.int32)
     nodes = np.zeros(wl.B, np.int64)
     matched = np.zeros(wl.B, np.int64)
     t0 = time.perf_counter()
-    for r in wl.requests:
+    for r in (wl.requests[i] for i in order):
         row, node, m = tree.admit(r.tokens, r.cached, r.new, out_row=table[r.row, :r.seq_len])
         nodes[r.row], matched[r.row] = node, m
         if r.cached > m:
@@ -299,20 +307,26 @@ def cpu_baseline(st, budget_s=20.0):
                       f"({toks} query tokens, {dt:.1f} s, KV regenerated per request, fp64 numpy)"}
 
 
-def measured_traffic(kernel, config):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a plain
-    copy's reading), or None when the kernel source has changed since they were taken or the workload
-    is not the one they were taken on."""
+EXTEND_KERNEL = "extend_bf16_kernel<128, false, 4, 2>"
+VERIFY_KERNEL = "extend_bf16_kernel<128, true, 4, 1>"
+DECODE_KERNEL = "decode_bf16_kernel<128>"
+MERGE_KERNEL = "decode_merge_kernel<128>"
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` ("5", "2", "3", "4", "verify") from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's reading), or None
+    when the kernel source has changed since they were taken or they do not cover the pair."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "hbm_traffic_mixed_batch.json")
-    if config != 5 or not os.path.exists(path):
+    path = os.path.join(here, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src = open(os.path.join(here, rec["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["sha256"] or kernel not in rec["kernels"]:
+    k = rec["workloads"].get(str(workload), {}).get("kernels", {}).get(kernel)
+    if hashlib.sha256(src).hexdigest() != rec["sha256"] or k is None:
         return None
-    k = rec["kernels"][kernel]
     return {"bytes": k["read_bytes"] + k["write_bytes"], "read": k["read_bytes"], "write": k["write_bytes"]}
 
 
@@ -395,7 +409,7 @@ def main():
     ext_tf = flops / (ext_ms / 1e3) / 1e12 if st.ext else 0.0
     dec_gbs = ub / (dec_ms / 1e3) / 1e9 if st.dec else 0.0
     if st.ext:
-        roof = {"bound": "mfma", "kernel": "extend_bf16_kernel<128, false>", "achieved": round(ext_tf, 2),
+        roof = {"bound": "mfma", "kernel": EXTEND_KERNEL, "achieved": round(ext_tf, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ext_tf / BF16_PEAK_TFLOPS, 4),
                 "traffic": None, "algorithmic_per_launch": flops, "avg_launch_ms": round(ext_ms, 4)}
         tr = measured_traffic(roof["kernel"], args.config)
@@ -404,7 +418,7 @@ def main():
             roof["traffic_unit"] = "bytes/launch (HBM read+write, rocprofv3 FETCH_SIZE+WRITE_SIZE)"
             roof["traffic_read_write"] = [tr["read"], tr["write"]]
     else:
-        roof = {"bound": "hbm", "kernel": "decode_bf16_kernel<128>", "achieved": round(dec_gbs, 1),
+        roof = {"bound": "hbm", "kernel": DECODE_KERNEL, "achieved": round(dec_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None, "algorithmic_per_launch": ub, "avg_launch_ms": round(dec_ms, 4)}
         tr = measured_traffic(roof["kernel"], args.config)
@@ -428,8 +442,10 @@ def main():
         out["decode_hbm"] = {"achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "unique_kv_bytes": ub,
                              "flat_kv_bytes": decode_flat_bytes(st)}
-        tr = measured_traffic("decode_bf16_kernel<128>", args.config)
+        tr = measured_traffic(DECODE_KERNEL, args.config)
+        trm = measured_traffic(MERGE_KERNEL, args.config)
         out["decode_hbm"]["traffic_decode_kernel"] = tr["bytes"] if tr is not None else None
+        out["decode_hbm"]["traffic_merge_kernel"] = trm["bytes"] if trm is not None else None
     if not args.no_extra:
         out["other_configs"] = extra_configs()
     if not args.no_cpu_baseline:
@@ -455,6 +471,9 @@ def extra_configs():
                       "unique_kv_bytes": ub, "hbm_gbs_unique": round(ub / (med / 1e3) / 1e9, 1),
                       "hbm_frac": round(ub / (med / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                       "tokens_per_s": round(len(st.dec) / (med / 1e3), 1)})
+            for name, kern in (("traffic_decode_kernel", DECODE_KERNEL), ("traffic_merge_kernel", MERGE_KERNEL)):
+                tr = measured_traffic(kern, cfg)
+                d[name] = tr["bytes"] if tr is not None else None
         if st.ext:
             med, _ = time_fn(lambda: run_extend(st), 20, 3, flush)
             f = extend_flops(st)
@@ -463,6 +482,8 @@ def extra_configs():
                       "tokens_per_s": round(st.ext_tokens / (med / 1e3), 1)})
             if st.wl.dtype == "bf16":
                 d["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+                tr = measured_traffic(EXTEND_KERNEL, cfg)
+                d["traffic_extend_kernel"] = tr["bytes"] if tr is not None else None
             else:                    # the fp32 path is a VALU kernel: against the fp32 vector peak
                 d["fp32_frac"] = round(tf / FP32_PEAK_TFLOPS, 4)
         res[str(cfg)] = d
@@ -550,8 +571,10 @@ def verify_extra(flush, B=256, prefix=32768, n=16, Hq=64, Hkv=8, D=128, seed=100
     ub = S * 2 * Hkv * D * 2
     depth1 = (pos - prefix + 1).astype(np.int64)          # keys seen among the verify tokens
     flops = int(((prefix + depth1).sum()) * Hq * 4 * D)
+    tr = measured_traffic(VERIFY_KERNEL, "verify")
     return {"workload": f"draft-tree verify ({B} x {prefix:,} cached + {n} verify tokens, random trees, bf16, "
                         f"GQA {Hq}/{Hkv}, d{D})",
+            "traffic_verify_kernel": tr["bytes"] if tr is not None else None,
             "verify_us": round(med * 1e3, 2), "unique_kv_bytes": ub,
             "hbm_gbs_unique": round(ub / (med / 1e3) / 1e9, 1),
             "hbm_frac": round(ub / (med / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
