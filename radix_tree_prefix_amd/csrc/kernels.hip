@@ -992,7 +992,9 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
 // Decode: kDecKB-key tiles through kDecNS LDS stages (kDecNS - 1 tiles in flight while one
 // is computed), up to two workgroups per CU.  Measured on the small decode batches and the
 // mixed batch: 32-key tiles through 4 or 5 stages (more bytes in flight, twice the waits and
-// barriers per key) are 4-10% slower than 64-key tiles through 2.
+// barriers per key) are 4-10% slower than 64-key tiles through 2; the same work items run on
+// the extend engine's pipeline (8 stages of 32 keys, 6 in flight, one workgroup per CU, which
+// streams the long verify batch at 71% of HBM bandwidth) are 3-38% slower.
 constexpr int kDecKB = 64, kDecNS = 2;
 struct DecodeArgs {
   const uint16_t* q;
