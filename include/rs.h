@@ -169,9 +169,14 @@ int64_t rs_evict(rs_tree* t, int64_t num_tokens);
 int rs_admit(rs_tree* t, const int32_t* tokens, int64_t cached, int64_t n_new,
              int32_t* out_row, int64_t* out_node, int64_t* out_matched);
 
+/* Counters of the tree [T "A tree, not a map": the tree keeps the tokens of unlocked nodes as
+ * evictable and those of locked nodes as protected, moving a node's length between the two
+ * when its lock_ref goes 0 <-> 1]: evictable and protected tokens, nodes, free slots, tokens
+ * evicted so far, the logical clock and match statistics (rs_stats_t).  RS_E_INVAL on NULL. */
 int rs_stats(const rs_tree* t, rs_stats_t* out);
 
-/* Canonical text of the tree (for tests): depth-first from the root, children in
+/* Canonical text of the tree, an inspection aid for tests (no passage defines a format; the
+ * fields printed are the pages' node fields [T "A tree, not a map"]): depth-first from the root, children in
  * ascending first-token order, one line per node
  * "depth id lock_ref last_access len | key tokens | slots\n".
  * Writes at most cap bytes (NUL-terminated if room) and the full size (excluding
@@ -286,11 +291,14 @@ void rs_plan_destroy(rs_plan* p);
 
 /* Workspace bytes rs_decode_attention needs: one partial (o, lse) per (work item,
  * request, query head) in fp32.  plan = NULL sizes the flat (one segment per request)
- * mode for B requests of up to max_seq_len tokens. */
+ * mode for B requests of up to max_seq_len tokens.  The pages define no workspace: it holds
+ * the per-chunk results that the log-sum-exp combine (written out at rs_decode_attention)
+ * joins, the structure that lets a shared segment be read once [L "How the runtime and
+ * frontend work together"]. */
 int64_t rs_decode_workspace_bytes(const rs_plan* p, int32_t B, int32_t max_seq_len,
                                   int32_t Hq, int32_t Hkv, int32_t D);
-/* Zero a workspace (a fill kernel on stream).  Optional: every partial the merge reads
- * is written first by the same rs_decode_attention call. */
+/* Zero a workspace (a fill kernel on stream; no passage defines it).  Optional: every partial
+ * the merge reads is written first by the same rs_decode_attention call. */
 int rs_decode_workspace_init(void* ws, int64_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ device ops */
@@ -322,7 +330,8 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool,
 
 /* Host: the request order for rs_extend_attention, longest causal work first
  * (work = extend_len * (prefix_len + (extend_len + 1) / 2); ties by index).  prefix_lens,
- * extend_lens: host int32 [B]; order: host int32 [B] out. */
+ * extend_lens: host int32 [B]; order: host int32 [B] out.  A launch-order aid of this
+ * library, not an operation of the pages: it changes when work starts, never a result. */
 int rs_extend_order(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t B, int32_t* order);
 
 /* ------------------------------------------------------------------ draft-tree verify */
@@ -416,7 +425,9 @@ int rs_decode_attention_noalloc(const void* q, const void* k_pool, const void* v
                                 const void* plan_dev, void* out, float* lse_out, void* stream);
 
 /* Merge two attention states over disjoint key sets (the combine step above), rows x D:
- * o_a, o_b, o: device [rows][D] of dtype; lse_*: device float [rows]. */
+ * o_a, o_b, o: device [rows][D] of dtype; lse_*: device float [rows].  The pages state no
+ * formula: this is the log-sum-exp identity that makes attention over a union of key sets
+ * from attention over its parts, exposed so that tests can check the combine on its own. */
 int rs_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                     int64_t rows, int32_t D, int32_t dtype, void* o, float* lse, void* stream);
 
