@@ -20,7 +20,9 @@
 //   lazily moved reference point;
 // * extend: 4 waves of 64 rows (tokens x heads) in two row blocks, 32-key tiles, a
 //   software-pipelined loop and a per-row reference fixed from the first tile.
-// fp32 runs a VALU path (one wave per query row).
+// fp32 extend runs the same operand scheme on 32x32x2 fp32 MFMAs with operands loaded
+// straight into registers (workgroups of 32 query rows, 4 waves splitting the keys); fp32
+// decode runs on the VALU (one wave per query row).
 
 #include <hip/hip_runtime.h>
 
@@ -1164,33 +1166,238 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ fp32 (VALU)
-// One wave per (request, query, head).  Query rows come either from an extend batch
-// (qo_indptr / prefix_lens / extend_lens) or from a decode batch (seq_lens).
+// ------------------------------------------------------------------ fp32 extend (matrix cores)
+// Extend attention in fp32 on v_mfma_f32_32x32x2_f32 (fp32 products, fp32 sums).  A
+// workgroup takes 32 query rows of one request and one KV head -- rows are (token, query
+// head of the group) pairs, token-major, as in the bf16 engines -- and its 4 waves split
+// the key range in 32-key tiles (wave w takes tiles w, w + 4, ...), each with its own
+// online softmax; the four partial states merge through LDS at the end.
+//
+// Same operand scheme as the bf16 engines, without LDS staging: each lane loads its own
+// operands straight from the pool.
+//     S^T = K Q^T:  step s (of D/2) -- lane l gives K[key l%32][dim (D/2)(l/32) + s] as A
+//                   and Q[row l%32][same dim] as B, so a lane's K row is D/2 adjacent floats;
+//     O^T += V^T P^T: accumulator register j of lane l is key 8(j/4) + 4(l/32) + j%4 for
+//                   row l%32, and step j of P V takes exactly those keys: P enters as B
+//                   unmoved; block c (of D/32) of the output holds dims (D/32) m + c for
+//                   accumulator row m, so a lane's V operands for one key are D/32 adjacent
+//                   floats of dims (D/32)(l%32) ...
+// A wave loads tile t + 4 (and the slot ids of tile t + 8) before it computes tile t.
+constexpr int kF32Rows = 32;     // query rows per workgroup
+constexpr int kF32Waves = 4;
+constexpr float kF32Slack = 8.f; // weights stay below 2^kF32Slack between moves of the reference
+
 template <int D>
-__global__ void __launch_bounds__(64) attn_f32_kernel(
+struct F32Kv {
+  float k[D / 2];          // key l%32, dims [(D/2)(l/32), (D/2)(l/32) + D/2)
+  float v[16][D / 32];     // step j: key 8(j/4) + 4(l/32) + j%4, dims (D/32)(l%32) + c
+};
+
+// Loads of one tile.  Lane l's key row (its K operand) starts at the byte offset of its slot;
+// the V operands of step j come from the row of key 8(j/4) + 4(l/32) + j%4, the same for
+// all lanes of a half, so the 32 row offsets go through a per-wave LDS table (one
+// broadcast read per step) instead of being recomputed from shuffled slot ids.
+template <int D>
+__device__ __forceinline__ void f32_kv_load(F32Kv<D>& t, const float* __restrict__ kb, const float* __restrict__ vb,
+                                            uint32_t stride, int32_t slot, int lane, uint64_t* vtab) {
+  const int h = lane >> 5, n = lane & 31;
+  const uint64_t row = uint64_t(uint32_t(slot)) * stride;   // slot ids are non-negative
+  const float4* kr = reinterpret_cast<const float4*>(kb + row + (D / 2) * h);
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const float4 x = kr[c];
+    t.k[4 * c + 0] = x.x;
+    t.k[4 * c + 1] = x.y;
+    t.k[4 * c + 2] = x.z;
+    t.k[4 * c + 3] = x.w;
+  }
+  if (h == 0) vtab[n] = row;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float* vr = vb + vtab[8 * (j / 4) + 4 * h + j % 4] + (D / 32) * n;
+    if constexpr (D == 64) {
+      const float2 x = *reinterpret_cast<const float2*>(vr);
+      t.v[j][0] = x.x;
+      t.v[j][1] = x.y;
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(vr);
+      t.v[j][0] = x.x;
+      t.v[j][1] = x.y;
+      t.v[j][2] = x.z;
+      t.v[j][3] = x.w;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One 32-key tile: scores, causal mask (keys past the row's position drop out), softmax
+// weights exp2(s - ref) in exp2 units (the scale and log2(e) are folded into the query), P V.
+// The reference ref of a row moves only when a score exceeds it by more than kF32Slack;
+// then the running sum and the output accumulators are rescaled (a wave-wide branch).
+template <int D>
+__device__ __forceinline__ void f32_tile(const F32Kv<D>& t, const float (&qv)[D / 2], int key0, int pos,
+                                         bool mask, int h, float& ref, float& lsum, f32x16 (&o)[D / 32]) {
+  f32x16 s = {};
+#pragma unroll
+  for (int st = 0; st < D / 2; ++st) s = __builtin_amdgcn_mfma_f32_32x32x2f32(t.k[st], qv[st], s, 0, 0, 0);
+  if (mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + 8 * (i / 4) + 4 * h + i % 4 > pos) s[i] = -INFINITY;
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  mx = xhalf_max(mx);
+  const bool move = mx > ref + kF32Slack;
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    const float alpha = move ? __builtin_amdgcn_exp2f(ref - mx) : 1.f;   // ref = -inf: 0
+    ref = move ? mx : ref;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) o[c] *= alpha;
+  }
+  const float r = ref == -INFINITY ? 0.f : ref;   // a row with no visible key yet
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = __builtin_amdgcn_exp2f(s[i] - r);
+    ps += s[i];
+  }
+  lsum += ps;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) o[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(t.v[j][c], s[j], o[c], 0, 0, 0);
+}
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) extend_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
     const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ qo_indptr,
-    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens,
-    const int32_t* __restrict__ seq_lens, int max_q, int max_len, int Hq, int Hkv, float sm_scale,
-    float* __restrict__ out, float* __restrict__ lse_out) {
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ extend_lens, int n_qtiles, int Hq, int Hkv,
+    float sm_scale, const int32_t* __restrict__ order, float* __restrict__ out) {
+  __shared__ float so[NW][D][kF32Rows + 1];   // partial O^T per wave, padded against bank conflicts
+  __shared__ float sm[NW][kF32Rows], sl[NW][kF32Rows];
+  __shared__ uint64_t vtab[NW][32];            // V row offsets of the tile being loaded, per wave
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = Hq / Hkv;
+  const int kvh = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  // requests in the given order; within a request the later (longer) q-tiles first
+  const int qt = n_qtiles - 1 - rest % n_qtiles, bi = rest / n_qtiles;
+  const int b = order ? order[bi] : bi;
+  const int R = extend_lens[b] * G, r0 = qt * kF32Rows;
+  if (r0 >= R) return;
+  const int prefix = prefix_lens[b], qo = qo_indptr[b];
+  const int r_last = min(r0 + kF32Rows, R) - 1;
+  const int nkeys = prefix + r_last / G + 1, nkt = (nkeys + 31) / 32;
+  const int pos_min = prefix + r0 / G;
+  // this lane's query row (rows past the request's end repeat its last row; never stored)
+  const int r = min(r0 + n, r_last);
+  const int pos = prefix + r / G;
+  const int64_t qoff = (int64_t(qo + r / G) * Hq + kvh * G + r % G) * D;
+  const float c = sm_scale * kLog2e;
+  float qv[D / 2];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(q + qoff + (D / 2) * h);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      const float4 x = qp[i];
+      qv[4 * i + 0] = x.x * c;
+      qv[4 * i + 1] = x.y * c;
+      qv[4 * i + 2] = x.z * c;
+      qv[4 * i + 3] = x.w * c;
+    }
+  }
+  const int32_t* trow = req_to_token + int64_t(b) * ld;
+  const uint32_t stride = uint32_t(Hkv) * D;
+  const float* kb = kpool + int64_t(kvh) * D;
+  const float* vb = vpool + int64_t(kvh) * D;
+  float ref = -INFINITY, lsum = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+  // key indexes past the context repeat its last key: always a real row, weight 0
+  auto slot_of = [&](int kt) { return trow[min(kt * 32 + n, nkeys - 1)]; };
+  if (wave < nkt) {
+    F32Kv<D> ta, tb;
+    int kt = wave;
+    int32_t sa = slot_of(kt);
+    f32_kv_load<D>(ta, kb, vb, stride, sa, lane, vtab[wave]);
+    int32_t sb = slot_of(kt + NW);
+    for (;;) {
+      sa = slot_of(kt + 2 * NW);
+      f32_kv_load<D>(tb, kb, vb, stride, sb, lane, vtab[wave]);
+      f32_tile<D>(ta, qv, kt * 32, pos, kt * 32 + 31 > pos_min, h, ref, lsum, o);
+      kt += NW;
+      if (kt >= nkt) break;
+      sb = slot_of(kt + 2 * NW);
+      f32_kv_load<D>(ta, kb, vb, stride, sa, lane, vtab[wave]);
+      f32_tile<D>(tb, qv, kt * 32, pos, kt * 32 + 31 > pos_min, h, ref, lsum, o);
+      kt += NW;
+      if (kt >= nkt) break;
+    }
+  }
+  // merge the waves' states
+  lsum = xhalf_sum(lsum);
+  if (h == 0) {
+    sm[wave][n] = ref;
+    sl[wave][n] = lsum;
+  }
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) so[wave][(D / 32) * (8 * (i / 4) + 4 * h + i % 4) + cb][n] = o[cb][i];
+  __syncthreads();
+  constexpr int kPerThread = D * kF32Rows / (64 * NW);   // output dims per thread
+  static_assert(kPerThread % 4 == 0, "float4 stores");
+  const int row = tid / (D / kPerThread), d0 = (tid % (D / kPerThread)) * kPerThread;
+  if (r0 + row > r_last) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][row]);
+  float e[NW], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    e[w] = sm[w][row] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][row] - M);
+    L = fmaf(e[w], sl[w][row], L);
+  }
+  const float inv = 1.f / L;
+  const int rr = r0 + row;
+  float* op = out + (int64_t(qo + rr / G) * Hq + kvh * G + rr % G) * D + d0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; i += 4) {
+    float4 x;
+    float* xs = reinterpret_cast<float*>(&x);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc = fmaf(e[w], so[w][d0 + i + k][row], acc);
+      xs[k] = acc * inv;
+    }
+    *reinterpret_cast<float4*>(op + i) = x;
+  }
+}
+
+// ------------------------------------------------------------------ fp32 decode (VALU)
+// One wave per (request, query head): 64 keys per step, a lane per key for the scores,
+// the whole wave over the head dims for P V.
+template <int D>
+__global__ void __launch_bounds__(64) decode_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
+    const int32_t* __restrict__ req_to_token, int64_t ld, const int32_t* __restrict__ seq_lens, int max_len, int Hq,
+    int Hkv, float sm_scale, float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int DPL = D / 64;                    // output dims per lane
   __shared__ float qs[D];
   const int lane = threadIdx.x;
-  const int h = blockIdx.x % Hq;
-  const int rest = blockIdx.x / Hq;
-  const int i = rest % max_q, b = rest / max_q;
-  int pos, qrow;
-  if (seq_lens) {
-    pos = min(seq_lens[b], max_len) - 1;      // decode: a request is cut to max_len keys
-    qrow = b;
-  } else {
-    if (i >= extend_lens[b]) return;
-    pos = prefix_lens[b] + i;
-    qrow = qo_indptr[b] + i;
-  }
+  const int h = blockIdx.x % Hq, b = blockIdx.x / Hq;
+  const int pos = min(seq_lens[b], max_len) - 1;   // a request is cut to max_len keys
   const int G = Hq / Hkv, kvh = h / G;
-  const float* qp = q + (int64_t(qrow) * Hq + h) * D;
+  const float* qp = q + (int64_t(b) * Hq + h) * D;
   for (int d = lane; d < D; d += 64) qs[d] = qp[d];
   __syncthreads();
   const int32_t* trow = req_to_token + int64_t(b) * ld;
@@ -1241,10 +1448,10 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(
     }
     m = m_new;
   }
-  float* op = out + (int64_t(qrow) * Hq + h) * D;
+  float* op = out + (int64_t(b) * Hq + h) * D;
 #pragma unroll
   for (int k = 0; k < DPL; ++k) op[lane + 64 * k] = o[k] / l;
-  if (lse_out && lane == 0) lse_out[int64_t(qrow) * Hq + h] = m + logf(l);
+  if (lse_out && lane == 0) lse_out[int64_t(b) * Hq + h] = m + logf(l);
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -1450,13 +1657,15 @@ int rs_extend_attention(const void* q, const void* k_pool, const void* v_pool, c
     return hip_check("rs_extend_attention");
   }
   if (dtype == RS_DTYPE_F32) {
-    const int64_t blocks = int64_t(B) * max_extend_len * Hq;
+    const int64_t rows = int64_t(max_extend_len) * (Hq / Hkv);
+    const int64_t n_qtiles = (rows + kF32Rows - 1) / kF32Rows;
+    const int64_t blocks = int64_t(B) * n_qtiles * Hkv;
     if (blocks > INT32_MAX) return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: grid too large");
-    auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
-    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64), 0, s, static_cast<const float*>(q),
+    auto kern = D == 128 ? extend_f32_kernel<128, kF32Waves> : extend_f32_kernel<64, kF32Waves>;
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(64 * kF32Waves), 0, s, static_cast<const float*>(q),
                        static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
-                       qo_indptr, prefix_lens, extend_lens, nullptr, max_extend_len, 0, Hq, Hkv, sm_scale,
-                       static_cast<float*>(out), nullptr);
+                       qo_indptr, prefix_lens, extend_lens, int(n_qtiles), Hq, Hkv, sm_scale, order,
+                       static_cast<float*>(out));
     return hip_check("rs_extend_attention");
   }
   return rs::fail(RS_E_UNSUPPORTED, "rs_extend_attention: dtype");
@@ -1475,11 +1684,10 @@ int rs_decode_attention(const void* q, const void* k_pool, const void* v_pool, c
   if (max_seq_len <= 0) return rs::fail(RS_E_INVAL, "rs_decode_attention: every request needs >= 1 key");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == RS_DTYPE_F32) {
-    auto kern = D == 128 ? attn_f32_kernel<128> : attn_f32_kernel<64>;
+    auto kern = D == 128 ? decode_f32_kernel<128> : decode_f32_kernel<64>;
     hipLaunchKernelGGL(kern, dim3(unsigned(int64_t(B) * Hq)), dim3(64), 0, s, static_cast<const float*>(q),
                        static_cast<const float*>(k_pool), static_cast<const float*>(v_pool), req_to_token, ld,
-                       nullptr, nullptr, nullptr, seq_lens, 1, max_seq_len, Hq, Hkv, sm_scale,
-                       static_cast<float*>(out), lse_out);
+                       seq_lens, max_seq_len, Hq, Hkv, sm_scale, static_cast<float*>(out), lse_out);
     return hip_check("rs_decode_attention");
   }
   if (dtype != RS_DTYPE_BF16) return rs::fail(RS_E_UNSUPPORTED, "rs_decode_attention: dtype");

@@ -168,7 +168,7 @@ def test_extend_f32_ragged(torch_rs, Hq, Hkv, D):
     assert err <= TOL["f32"], err
 
 
-def _planted_case(torch, rs, sm, lens, seed):
+def _planted_case(torch, rs, sm, lens, seed, dtname="bf16"):
     """Extend where one late key of each request is a scaled copy of its first query row,
     so that row's late score stands far above every score of the first key tile."""
     Hq, Hkv, D = 8, 2, 128
@@ -188,8 +188,9 @@ def _planted_case(torch, rs, sm, lens, seed):
         off += n
         p = lens[b][0]
         kp[table[b, p - 7]] = q[qo[b], 0:Hq:Hq // Hkv]     # key p-7 of KV head h = query 0's head h*G
-    out = rs.extend_attention(_to_dev(torch, q, torch.bfloat16), _to_dev(torch, kp, torch.bfloat16),
-                              _to_dev(torch, vp, torch.bfloat16), _to_dev(torch, table, torch.int32),
+    dt = torch.bfloat16 if dtname == "bf16" else torch.float32
+    out = rs.extend_attention(_to_dev(torch, q, dt), _to_dev(torch, kp, dt),
+                              _to_dev(torch, vp, dt), _to_dev(torch, table, torch.int32),
                               _to_dev(torch, qo, torch.int32),
                               _to_dev(torch, np.array([p for p, _ in lens], np.int32), torch.int32),
                               _to_dev(torch, ext, torch.int32), int(ext.max()), sm)
@@ -212,6 +213,17 @@ def test_extend_late_dominant_key(torch_rs, sm):
     _say(f"extend planted dominant key sm_scale={sm} lens={lens}")
     err = _planted_case(torch, rs, sm, lens, seed=11)
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("sm", [0.35, 1.0])
+def test_extend_f32_late_dominant_key(torch_rs, sm):
+    """The fp32 path on the same planted batch: the softmax reference of the affected rows
+    has to move on a late tile (scores ~65 or ~185 log2-units above the first tile's)."""
+    torch, rs = torch_rs
+    lens = [(100, 50), (700, 37), (3000, 64)]
+    _say(f"extend f32 planted dominant key sm_scale={sm} lens={lens}")
+    err = _planted_case(torch, rs, sm, lens, seed=11, dtname="f32")
+    assert err <= TOL["f32"], err
 
 
 def test_extend_prefix_zero_is_textbook_causal(torch_rs):
@@ -489,12 +501,14 @@ def test_config5_every_extend_request(mixed_batch, half):
     assert not bad, bad
 
 
-def test_extend_order_changes_no_result(torch_rs):
-    """The longest-first start order only reorders workgroups: outputs are bit-identical."""
+@pytest.mark.parametrize("cfg", [3, 1])
+def test_extend_order_changes_no_result(torch_rs, cfg):
+    """The longest-first start order only reorders workgroups: outputs are bit-identical
+    (bf16 engine on the multi-step agent, fp32 kernel on the two-document agent)."""
     torch, rs = torch_rs
-    _say("config 3 extend with and without the work order")
+    _say(f"config {cfg} extend with and without the work order")
     b = _bench()
-    st = b.setup(3)
+    st = b.setup(cfg)
     b.run_store(st)
     b.run_extend(st)
     with_order = st.out_ext.clone()
