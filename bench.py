@@ -36,7 +36,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector alike)
 
 
 # ---------------------------------------------------------------------------- setup
@@ -311,6 +311,7 @@ EXTEND_KERNEL = "extend_bf16_kernel<128, false, 4, 2>"
 VERIFY_KERNEL = "extend_bf16_kernel<128, true, 4, 1>"
 DECODE_KERNEL = "decode_bf16_kernel<128>"
 MERGE_KERNEL = "decode_merge_kernel<128>"
+F32_KERNEL = "extend_f32_kernel<64, 4>"
 
 
 def code_hash(path):
@@ -325,7 +326,7 @@ def code_hash(path):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` ("5", "2", "3", "4", "verify") from the
+    """HBM bytes per launch of `kernel` on `workload` ("5", "1", "2", "3", "4", "verify") from the
     committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's reading), or None
     when the kernel source has changed since they were taken or they do not cover the pair."""
     here = os.path.dirname(os.path.abspath(__file__))
@@ -493,8 +494,10 @@ def extra_configs():
                 d["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
                 tr = measured_traffic(EXTEND_KERNEL, cfg)
                 d["traffic_extend_kernel"] = tr["bytes"] if tr is not None else None
-            else:                    # the fp32 path is a VALU kernel: against the fp32 vector peak
+            else:                    # fp32 on 32x32x2 fp32 MFMAs: against the fp32 matrix peak
                 d["fp32_frac"] = round(tf / FP32_PEAK_TFLOPS, 4)
+                tr = measured_traffic(F32_KERNEL, cfg)
+                d["traffic_extend_kernel"] = tr["bytes"] if tr is not None else None
         res[str(cfg)] = d
         del st
         torch.cuda.empty_cache()

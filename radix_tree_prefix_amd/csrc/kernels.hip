@@ -1183,9 +1183,19 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
 //                   accumulator row m, so a lane's V operands for one key are D/32 adjacent
 //                   floats of dims (D/32)(l%32) ...
 // A wave loads tile t + 4 (and the slot ids of tile t + 8) before it computes tile t.
+//
+// Softmax reference, as in the bf16 extend engine: a wave fixes each row's reference at
+// the row's maximum in the first tile the wave computes and never moves it, so the loop
+// tracks no maximum and never rescales O (the VALU work of a tile is the exp2 and the row
+// sums; measured on gfx950, fp32 MFMAs leave little VALU issue alongside them).  The
+// reference enters the scores through the accumulator: the QK chain starts from -ref,
+// so its result is already s - ref.  Later weights above 1 are exact in fp32 until
+// they near 2^128; a wave whose row sum passes 2^100, or whose O is not finite, makes
+// the workgroup find every row's true maximum in a second pass and recompute with it
+// (all weights <= 1).
 constexpr int kF32Rows = 32;     // query rows per workgroup
 constexpr int kF32Waves = 4;
-constexpr float kF32Slack = 8.f; // weights stay below 2^kF32Slack between moves of the reference
+constexpr float kF32SumLimit = 0x1p100f;   // above this a wave's row sum counts as overflowing
 
 template <int D>
 struct F32Kv {
@@ -1231,38 +1241,51 @@ __device__ __forceinline__ void f32_kv_load(F32Kv<D>& t, const float* __restrict
   __builtin_amdgcn_wave_barrier();
 }
 
-// One 32-key tile: scores, causal mask (keys past the row's position drop out), softmax
-// weights exp2(s - ref) in exp2 units (the scale and log2(e) are folded into the query), P V.
-// The reference ref of a row moves only when a score exceeds it by more than kF32Slack;
-// then the running sum and the output accumulators are rescaled (a wave-wide branch).
-template <int D>
+// What one pass over a wave's tiles computes.
+enum F32Mode {
+  kF32First = 0,   // weights against a reference fixed from the wave's first tile
+  kF32Track = 1,   // only each row's maximum score
+  kF32Fixed = 2,   // weights against a given reference (the row's true maximum)
+};
+
+// One 32-key tile: scores minus the reference (the chain starts from -ref), causal mask
+// (keys past the row's position drop out), then by mode: the running maximum, or the
+// weights exp2(s - ref) in exp2 units (the scale and log2(e) are folded into the query),
+// their row sums and P V.
+template <int D, int MODE>
 __device__ __forceinline__ void f32_tile(const F32Kv<D>& t, const float (&qv)[D / 2], int key0, int pos,
-                                         bool mask, int h, float& ref, float& lsum, f32x16 (&o)[D / 32]) {
-  f32x16 s = {};
+                                         bool mask, int h, bool& first, f32x16& negref, float& ref, float& lsum,
+                                         float& mx, f32x16 (&o)[D / 32]) {
+  f32x16 s = __builtin_amdgcn_mfma_f32_32x32x2f32(t.k[0], qv[0], negref, 0, 0, 0);
 #pragma unroll
-  for (int st = 0; st < D / 2; ++st) s = __builtin_amdgcn_mfma_f32_32x32x2f32(t.k[st], qv[st], s, 0, 0, 0);
+  for (int st = 1; st < D / 2; ++st) s = __builtin_amdgcn_mfma_f32_32x32x2f32(t.k[st], qv[st], s, 0, 0, 0);
   if (mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (key0 + 8 * (i / 4) + 4 * h + i % 4 > pos) s[i] = -INFINITY;
   }
-  float mx = s[0];
+  if (MODE == kF32Track) {
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = xhalf_max(mx);
-  const bool move = mx > ref + kF32Slack;
-  if (__builtin_amdgcn_ballot_w64(move)) {
-    const float alpha = move ? __builtin_amdgcn_exp2f(ref - mx) : 1.f;   // ref = -inf: 0
-    ref = move ? mx : ref;
-    lsum *= alpha;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) o[c] *= alpha;
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    return;
   }
-  const float r = ref == -INFINITY ? 0.f : ref;   // a row with no visible key yet
+  if (MODE == kF32First && first) {   // wave-uniform: the wave's first tile sets the reference
+    float m = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, s[i]);
+    ref = xhalf_max(m);
+    const float r = ref == -INFINITY ? 0.f : ref;   // no visible key: none in later tiles either
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] -= r;
+      negref[i] = -r;
+    }
+    first = false;
+  }
   float ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    s[i] = __builtin_amdgcn_exp2f(s[i] - r);
+    s[i] = __builtin_amdgcn_exp2f(s[i]);
     ps += s[i];
   }
   lsum += ps;
@@ -1270,6 +1293,45 @@ __device__ __forceinline__ void f32_tile(const F32Kv<D>& t, const float (&qv)[D 
   for (int j = 0; j < 16; ++j)
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) o[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(t.v[j][c], s[j], o[c], 0, 0, 0);
+}
+
+// Per-wave state of one query-row tile and the walk over the wave's key tiles.
+struct F32Walk {
+  const int32_t* trow;
+  const float* kb;
+  const float* vb;
+  uint32_t stride;
+  int nkeys, nkt, pos, pos_min, lane, wave, h, n;
+};
+
+template <int D, int NW, int MODE>
+__device__ __forceinline__ void f32_pass(const F32Walk& w, const float (&qv)[D / 2], uint64_t* tab, float& ref,
+                                         float& lsum, float& mx, f32x16 (&o)[D / 32]) {
+  if (w.wave >= w.nkt) return;
+  // key indexes past the context repeat its last key: always a real row, weight 0
+  auto slot_of = [&](int kt) { return w.trow[min(kt * 32 + w.n, w.nkeys - 1)]; };
+  bool first = MODE == kF32First;
+  f32x16 negref;
+  const float r0 = MODE == kF32Fixed && ref != -INFINITY ? -ref : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negref[i] = r0;
+  F32Kv<D> ta, tb;
+  int kt = w.wave;
+  int32_t sa = slot_of(kt);
+  f32_kv_load<D>(ta, w.kb, w.vb, w.stride, sa, w.lane, tab);
+  int32_t sb = slot_of(kt + NW);
+  for (;;) {
+    sa = slot_of(kt + 2 * NW);
+    f32_kv_load<D>(tb, w.kb, w.vb, w.stride, sb, w.lane, tab);
+    f32_tile<D, MODE>(ta, qv, kt * 32, w.pos, kt * 32 + 31 > w.pos_min, w.h, first, negref, ref, lsum, mx, o);
+    kt += NW;
+    if (kt >= w.nkt) break;
+    sb = slot_of(kt + 2 * NW);
+    f32_kv_load<D>(ta, w.kb, w.vb, w.stride, sa, w.lane, tab);
+    f32_tile<D, MODE>(tb, qv, kt * 32, w.pos, kt * 32 + 31 > w.pos_min, w.h, first, negref, ref, lsum, mx, o);
+    kt += NW;
+    if (kt >= w.nkt) break;
+  }
 }
 
 template <int D, int NW>
@@ -1293,11 +1355,21 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_f32_kernel(
   if (r0 >= R) return;
   const int prefix = prefix_lens[b], qo = qo_indptr[b];
   const int r_last = min(r0 + kF32Rows, R) - 1;
-  const int nkeys = prefix + r_last / G + 1, nkt = (nkeys + 31) / 32;
-  const int pos_min = prefix + r0 / G;
+  F32Walk w;
+  w.nkeys = prefix + r_last / G + 1;
+  w.nkt = (w.nkeys + 31) / 32;
+  w.pos_min = prefix + r0 / G;
   // this lane's query row (rows past the request's end repeat its last row; never stored)
   const int r = min(r0 + n, r_last);
-  const int pos = prefix + r / G;
+  w.pos = prefix + r / G;
+  w.lane = lane;
+  w.wave = wave;
+  w.h = h;
+  w.n = n;
+  w.trow = req_to_token + int64_t(b) * ld;
+  w.stride = uint32_t(Hkv) * D;
+  w.kb = kpool + int64_t(kvh) * D;
+  w.vb = vpool + int64_t(kvh) * D;
   const int64_t qoff = (int64_t(qo + r / G) * Hq + kvh * G + r % G) * D;
   const float c = sm_scale * kLog2e;
   float qv[D / 2];
@@ -1312,37 +1384,39 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_f32_kernel(
       qv[4 * i + 3] = x.w * c;
     }
   }
-  const int32_t* trow = req_to_token + int64_t(b) * ld;
-  const uint32_t stride = uint32_t(Hkv) * D;
-  const float* kb = kpool + int64_t(kvh) * D;
-  const float* vb = vpool + int64_t(kvh) * D;
-  float ref = -INFINITY, lsum = 0.f;
+  float ref = -INFINITY, lsum = 0.f, mx = -INFINITY;
   f32x16 o[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
-  // key indexes past the context repeat its last key: always a real row, weight 0
-  auto slot_of = [&](int kt) { return trow[min(kt * 32 + n, nkeys - 1)]; };
-  if (wave < nkt) {
-    F32Kv<D> ta, tb;
-    int kt = wave;
-    int32_t sa = slot_of(kt);
-    f32_kv_load<D>(ta, kb, vb, stride, sa, lane, vtab[wave]);
-    int32_t sb = slot_of(kt + NW);
-    for (;;) {
-      sa = slot_of(kt + 2 * NW);
-      f32_kv_load<D>(tb, kb, vb, stride, sb, lane, vtab[wave]);
-      f32_tile<D>(ta, qv, kt * 32, pos, kt * 32 + 31 > pos_min, h, ref, lsum, o);
-      kt += NW;
-      if (kt >= nkt) break;
-      sb = slot_of(kt + 2 * NW);
-      f32_kv_load<D>(ta, kb, vb, stride, sa, lane, vtab[wave]);
-      f32_tile<D>(tb, qv, kt * 32, pos, kt * 32 + 31 > pos_min, h, ref, lsum, o);
-      kt += NW;
-      if (kt >= nkt) break;
-    }
+  // O stays in AGPRs through the loop: only MFMAs touch it there
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) asm volatile("" : "+a"(o[cb]));
+  f32_pass<D, NW, kF32First>(w, qv, vtab[wave], ref, lsum, mx, o);
+  // overflow: a row sum past the limit, or an O that is not finite (x * 0 is NaN exactly
+  // for inf and NaN)
+  float z = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z = fmaf(o[cb][i], 0.f, z);
+  lsum = xhalf_sum(lsum);
+  if (__syncthreads_or(!(lsum <= kF32SumLimit) || z != 0.f)) {
+    // every row's true maximum over all keys, then the weights again against it
+    f32_pass<D, NW, kF32Track>(w, qv, vtab[wave], ref, lsum, mx, o);
+    mx = xhalf_max(mx);
+    if (h == 0) sm[wave][n] = mx;
+    __syncthreads();
+    ref = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) ref = fmaxf(ref, sm[v][n]);
+    __syncthreads();
+    lsum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+    f32_pass<D, NW, kF32Fixed>(w, qv, vtab[wave], ref, lsum, mx, o);
+    lsum = xhalf_sum(lsum);
   }
   // merge the waves' states
-  lsum = xhalf_sum(lsum);
   if (h == 0) {
     sm[wave][n] = ref;
     sl[wave][n] = lsum;
@@ -1358,14 +1432,17 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_f32_kernel(
   if (r0 + row > r_last) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][row]);
+  for (int v = 0; v < NW; ++v) M = fmaxf(M, sm[v][row]);
   float e[NW], L = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    e[w] = sm[w][row] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][row] - M);
-    L = fmaf(e[w], sl[w][row], L);
+  for (int v = 0; v < NW; ++v) {
+    e[v] = sm[v][row] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[v][row] - M);
+    L = fmaf(e[v], sl[v][row], L);
   }
+  // each wave's weight share first: e_w / L times a finite O_w cannot overflow
   const float inv = 1.f / L;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) e[v] *= inv;
   const int rr = r0 + row;
   float* op = out + (int64_t(qo + rr / G) * Hq + kvh * G + rr % G) * D + d0;
 #pragma unroll
@@ -1376,8 +1453,8 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_f32_kernel(
     for (int k = 0; k < 4; ++k) {
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc = fmaf(e[w], so[w][d0 + i + k][row], acc);
-      xs[k] = acc * inv;
+      for (int v = 0; v < NW; ++v) acc = fmaf(e[v], so[v][d0 + i + k][row], acc);
+      xs[k] = acc;
     }
     *reinterpret_cast<float4*>(op + i) = x;
   }
