@@ -898,6 +898,55 @@ __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool 
   return z != 0.f;                 // true for NaN
 }
 
+// The rows of one workgroup (RB 32-row blocks per wave, row = 32 (RB wave + block) + lane
+// % 32, tokens-major: token row / G, query head row % G of the KV head's group), their
+// passes over the keys and their outputs.
+template <int D, bool TREE, int NW, int RB>
+__device__ __forceinline__ void ext_rows(ExtShared<D, NW>& sh, ExtStream<D, NW>& a, const uint16_t* __restrict__ q,
+                                         uint16_t* __restrict__ out, const uint64_t* __restrict__ tree_mask, int wave,
+                                         int lane, int G, int Hq, int kvh, int qo, int t0, int ntok) {
+  bf16x8 qf[RB][D / 16];
+  int64_t qrow_idx[RB];
+  bool valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave * 32 * RB + rb * 32 + (lane & 31);
+    const int t = row / G, g = row % G;
+    valid[rb] = t < ntok;
+    qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
+    load_q<D>(qf[rb], q + qrow_idx[rb] * D, valid[rb], lane);
+    a.lim[rb] = valid[rb] ? a.tree_base + t0 + t : -1;
+    a.tm[rb] = (a.tree && valid[rb]) ? tree_mask[qo + t0 + t] : 0ull;
+  }
+  const ExtOffsets<D> off = ext_offsets<D>(lane);
+  ExtState<D, RB> es;
+  ext_reset<D, RB>(es);
+  // Q fragments and O accumulators live in AGPRs through the loop: only MFMAs read
+  // them there, which leaves the VGPRs to the scores, weights and addresses.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[rb][ks]));
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
+  }
+  for (int pass = 0;; ++pass) {
+    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0);
+    const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
+    if (pass == 1 || !__syncthreads_or(overflow)) break;
+    // Some weight overflowed: find each row's true maximum, then recompute the rows
+    // with it as the reference (the outputs above are overwritten).
+    ext_reset<D, RB>(es);
+    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true);
+    float mx[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
+    ext_reset<D, RB>(es);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) es.mc[rb] = (mx[rb] == -INFINITY ? 0.f : mx[rb]) * a.c;
+  }
+}
+
 // TREE: draft-tree verify (tree_mask gives each row's ancestor mask); otherwise causal.
 // NW waves per workgroup: 4 (one per SIMD; 64 rows each in the causal kernel, 32 in the
 // verify kernel) or 8 (two per SIMD, 32 rows each).  The launchers use 4: on the mixed
@@ -933,19 +982,6 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
   ExtStream<D, NW> a;
   a.tree = TREE;
   a.tree_base = prefix;
-  bf16x8 qf[RB][D / 16];
-  int64_t qrow_idx[RB];
-  bool valid[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = wave * 32 * RB + rb * 32 + (lane & 31);
-    const int t = row / G, g = row % G;
-    valid[rb] = row < tpb * G && t < ntok;
-    qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
-    load_q<D>(qf[rb], q + qrow_idx[rb] * D, valid[rb], lane);
-    a.lim[rb] = valid[rb] ? prefix + t0 + t : -1;
-    a.tm[rb] = (a.tree && valid[rb]) ? tree_mask[qo + t0 + t] : 0ull;
-  }
   a.kc = reinterpret_cast<const char*>(kpool + int64_t(kvh) * D);
   a.vc = reinterpret_cast<const char*>(vpool + int64_t(kvh) * D);
   a.trow = req_to_token + int64_t(b) * ld;
@@ -961,33 +997,16 @@ __global__ void __launch_bounds__(64 * NW, 1) extend_bf16_kernel(
   a.ntiles = (a.k1 + kExtKB - 1) / kExtKB;
   a.mask_from = a.tree ? prefix : prefix + t0 + 1;   // keys below this are visible to every row
   a.c = sm_scale * kLog2e;
-  const ExtOffsets<D> off = ext_offsets<D>(lane);
-  ExtState<D, RB> es;
-  ext_reset<D, RB>(es);
-  // Q fragments and O accumulators live in AGPRs through the loop: only MFMAs read
-  // them there, which leaves the VGPRs to the scores, weights and addresses.
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qf[rb][ks]));
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
+  // A request's last q-tile may hold few tokens.  When its rows fit in one 32-row block
+  // per wave, the workgroup runs the one-block loop: half the matrix and vector work per
+  // key tile for the same keys (the rows past the tile's tokens would be all masked).
+  if constexpr (!TREE && RB == 2) {
+    if (ntok * G <= NW * 32) {
+      ext_rows<D, TREE, NW, 1>(sh, a, q, out, tree_mask, wave, lane, G, Hq, kvh, qo, t0, ntok);
+      return;
+    }
   }
-  for (int pass = 0;; ++pass) {
-    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0);
-    const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
-    if (pass == 1 || !__syncthreads_or(overflow)) break;
-    // Some weight overflowed: find each row's true maximum, then recompute the rows
-    // with it as the reference (the outputs above are overwritten).
-    ext_reset<D, RB>(es);
-    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true);
-    float mx[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
-    ext_reset<D, RB>(es);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) es.mc[rb] = (mx[rb] == -INFINITY ? 0.f : mx[rb]) * a.c;
-  }
+  ext_rows<D, TREE, NW, RB>(sh, a, q, out, tree_mask, wave, lane, G, Hq, kvh, qo, t0, ntok);
 }
 
 // ------------------------------------------------------------------ decode (bf16)
