@@ -419,8 +419,9 @@ def main():
     ext_tf = flops / (ext_ms / 1e3) / 1e12 if st.ext else 0.0
     dec_gbs = ub / (dec_ms / 1e3) / 1e9 if st.dec else 0.0
     if st.ext:
-        roof = {"bound": "mfma", "kernel": EXTEND_KERNEL, "achieved": round(ext_tf, 2),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ext_tf / BF16_PEAK_TFLOPS, 4),
+        kern, peak = (EXTEND_KERNEL, BF16_PEAK_TFLOPS) if st.wl.dtype == "bf16" else (F32_KERNEL, FP32_PEAK_TFLOPS)
+        roof = {"bound": "mfma", "kernel": kern, "achieved": round(ext_tf, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(ext_tf / peak, 4),
                 "traffic": None, "algorithmic_per_launch": flops, "avg_launch_ms": round(ext_ms, 4)}
         tr = measured_traffic(roof["kernel"], args.config)
         if tr is not None:
