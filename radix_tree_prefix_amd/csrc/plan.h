@@ -13,7 +13,12 @@ constexpr int32_t kItemWords = 8;            // k0, k1, rep_row, n_req, req_off,
 constexpr int32_t kItemReqWords = 4;         // request, partial index, partials of the request, -
 constexpr int32_t kMaxRowsPerItem = 128;     // 4 waves x 32 query rows
 constexpr int32_t kFlatChunk = 256;          // keys per item in the flat (plan-less) mode
-constexpr int64_t kDecodeItemsTarget = 1024; // items x KV heads the chunk size aims for (fewer, longer items pay fewer workgroup start-ups)
+// items x KV heads the chunk size aims for: three quarters of the 512 decode workgroups the
+// chip holds at once (two per CU), so every item starts in the first round and fewer, longer
+// items pay fewer start-ups.  Measured against 1024 / 512 / 256: mixed batch 661 vs 671 / 661 /
+// 663 us, preamble agent 25.4 vs 27.3 / 26.8 / 27.4 us, tree of thought 63.2 vs 71.4 / 63.3 /
+// 71.2 us.
+constexpr int64_t kDecodeItemsTarget = 384;
 constexpr int64_t kMinChunk = 256;           // >= 4 tiles per item (shorter ones measured slower on the small batches)
 constexpr int64_t kMaxChunk = 8192;
 constexpr int32_t kChunkAlign = 64;          // item key ranges start at multiples of this (whole decode tiles)
