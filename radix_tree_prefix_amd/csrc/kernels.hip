@@ -528,7 +528,6 @@ __device__ __forceinline__ KFrags<D> ext_read_k(const char* kst, const ExtOffset
 }
 
 // S^T of both row blocks (results in the MFMA's accumulation registers).
-// S^T of both row blocks (results in the MFMA's accumulation registers).
 template <int D, int RB>
 __device__ __forceinline__ void ext_qk(f32x16 (&sc)[RB], const KFrags<D>& kf, const bf16x8 (&qf)[RB][D / 16]) {
 #pragma unroll
