@@ -1201,7 +1201,7 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
 // workgroup takes 32 query rows of one request and one KV head -- rows are (token, query
 // head of the group) pairs, token-major, as in the bf16 engines -- and its 4 waves split
 // the key range in 32-key tiles (wave w takes tiles w, w + 4, ...), each with its own
-// online softmax; the four partial states merge through LDS at the end.
+// softmax state (reference, row sums, O); the four states merge through LDS at the end.
 //
 // Same operand scheme as the bf16 engines, without LDS staging: each lane loads its own
 // operands straight from the pool.
