@@ -159,7 +159,7 @@ def test_extend_bf16_ragged(torch_rs, Hq, Hkv, D):
     assert err <= TOL["bf16"], err
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (8, 2, 128), (24, 8, 64), (64, 4, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (8, 2, 128), (24, 8, 64), (64, 4, 128), (128, 1, 64)])
 def test_extend_f32_ragged(torch_rs, Hq, Hkv, D):
     torch, rs = torch_rs
     lens = [(0, 1), (0, 70), (65, 3), (130, 64), (333, 0)]
