@@ -468,9 +468,12 @@ constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
 constexpr int kExtRows = 256;        // query rows per workgroup of the causal kernel: 4 waves x 64
 constexpr int kVerifyRows = 128;     // of the draft-tree verify kernel: 4 waves x 32
 constexpr int kExtAhead = kExtNS - 2;            // tiles in flight ahead of the math
-constexpr int kExtSlotLead = 2 * kExtAhead + 1;  // slot ids are loaded this many tiles ahead
-constexpr int kExtRing = 16;                     // slot-id ring entries (tiles)
-static_assert(kExtRing >= kExtSlotLead && kExtRing > kExtAhead, "slot ring too small");
+// Slot ids reach LDS in groups: one 64-lane dword DMA per wave brings its kExtKB/NW ids of
+// kExtRingGroup<NW> consecutive tiles, one group kExtRingGroup iterations before its first
+// use, into a ring of two groups.
+template <int NW>
+constexpr int kExtRingGroup = 64 / (kExtKB / NW);
+static_assert(kExtRingGroup<4> > kExtAhead - 1 && kExtRingGroup<8> > kExtAhead - 1, "slot group too small");
 
 // RB: 32-row blocks per wave (2 in the causal kernel, 1 in the verify kernel).
 template <int D, int RB>
@@ -640,7 +643,7 @@ struct ExtStream {
 template <int D, int NW>
 struct ExtShared {
   Stage<D, kExtKB> st[kExtNS];
-  int32_t ring[kExtRing][NW][kExtKB / NW];   // per tile and wave: its slot ids
+  int32_t ring[NW][2 * kExtRingGroup<NW>][kExtKB / NW];   // per wave and tile: its slot ids
 };
 
 // Global -> LDS loads issued through inline assembly.  The LDS address goes through M0,
@@ -666,16 +669,15 @@ __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {    // l
 }
 #pragma clang diagnostic pop
 
-// Slot ids of tile x into this wave's ring row: lane l < 8 loads the id of key 8*wave + l;
-// keys past k1 repeat the last slot.
+// Slot ids of tile group k (tiles kG .. kG+G-1, G = kExtRingGroup) into this wave's half of
+// the ring: lane l loads the id of key kExtKB (kG + l / P) + P wave + l % P (P = kExtKB / NW,
+// the wave's keys of a tile); keys past k1 repeat the last slot.
 template <int D, int NW>
-__device__ __forceinline__ void ext_slot_dma(ExtShared<D, NW>& sh, const ExtStream<D, NW>& a, int x) {
-  constexpr int kPerWave = kExtKB / NW;
-  // lanes 0 .. kPerWave-1 load (one instruction per wave all the same, so the waits count)
-  if (a.lane < kPerWave) {
-    const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * kPerWave + a.lane, a.k1 - 1);
-    dma_b32(src, lds_addr(&sh.ring[x % kExtRing][a.wave_u][0]));
-  }
+__device__ __forceinline__ void ext_slot_dma(ExtShared<D, NW>& sh, const ExtStream<D, NW>& a, int k) {
+  constexpr int P = kExtKB / NW, G = kExtRingGroup<NW>;
+  const int x = k * G + a.lane / P;
+  const int32_t* src = a.trow + min(x * kExtKB + a.wave_u * P + a.lane % P, a.k1 - 1);
+  dma_b32(src, lds_addr(&sh.ring[a.wave_u][(k & 1) * G][0]));
 }
 
 // This lane's slot id for each of its DMA instructions of tile x, from the ring.
@@ -689,7 +691,7 @@ __device__ __forceinline__ ExtRowSlots<D, NW> ext_read_slots(const ExtShared<D, 
   using L = StageLayout<D, kExtKB, NW>;
   ExtRowSlots<D, NW> r;
 #pragma unroll
-  for (int g = 0; g < L::kInstPerWave; ++g) r.s[g] = sh.ring[x % kExtRing][a.wave_u][g * L::kRowsPerInst + a.jrow];
+  for (int g = 0; g < L::kInstPerWave; ++g) r.s[g] = sh.ring[a.wave_u][x % (2 * kExtRingGroup<NW>)][g * L::kRowsPerInst + a.jrow];
   return r;
 }
 
@@ -707,14 +709,15 @@ __device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStrea
 }
 
 // Wait until tile t has landed for the whole workgroup (this wave's loads, then a
-// barrier).  Every iteration issues, in this order or not, one slot-id load and the tile
-// kExtAhead ahead (2*kInstPerWave loads; past the last tile they reload its last row into
-// a stage nobody reads), and loads complete in issue order: after tile t's loads come
-// those of the kExtAhead - 1 iterations since, so at most kAfter may stay outstanding.
-// Tiles issued before the loop wait for all.
+// barrier).  Every iteration issues the tile kExtAhead ahead (2*kInstPerWave loads; past
+// the last tile they reload its last row into a stage nobody reads) and, one iteration in
+// kExtRingGroup, a slot-id group; loads complete in issue order: after tile t's loads come
+// at least those of the kExtAhead - 1 iterations since, so kAfter may stay outstanding
+// (a slot-id load among them only makes the wait longer).  Tiles issued before the loop
+// wait for all.
 template <int D, int NW>
 __device__ __forceinline__ void ext_wait(int t) {
-  constexpr int kAfter = (kExtAhead - 1) * (1 + 2 * StageLayout<D, kExtKB, NW>::kInstPerWave);
+  constexpr int kAfter = (kExtAhead - 1) * 2 * StageLayout<D, kExtKB, NW>::kInstPerWave;
   static_assert(kAfter < 64, "vmcnt is 6 bits");
   if (t >= kExtAhead) wait_vmcnt_barrier<kAfter>();
   else wait_vmcnt_barrier<0>();
@@ -722,10 +725,12 @@ __device__ __forceinline__ void ext_wait(int t) {
 
 // Iteration t of the loop waits for tile t + 1 (its K is read ahead, at the end of
 // iteration t).  Tile t + 1 was issued by iteration t + 1 - kExtAhead (iteration 0 being
-// the tile-0 step), and kExtAhead - 2 iterations' loads came after it.
+// the tile-0 step), and kExtAhead - 2 iterations' loads came after it.  Everything issued
+// in iteration t + 1 - kExtAhead or earlier has then landed; that covers slot-id group k,
+// issued in iteration kG - kExtAhead - G and first read in iteration kG - kExtAhead.
 template <int D, int NW>
 __device__ __forceinline__ void ext_wait_next(int t) {
-  constexpr int kAfter = (kExtAhead - 2) * (1 + 2 * StageLayout<D, kExtKB, NW>::kInstPerWave);
+  constexpr int kAfter = (kExtAhead - 2) * 2 * StageLayout<D, kExtKB, NW>::kInstPerWave;
   if (t + 1 >= kExtAhead) wait_vmcnt_barrier<kAfter>();
   else wait_vmcnt_barrier<0>();
 }
@@ -769,7 +774,11 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
                                          int t) {
   ext_wait_next<D, NW>(t);
   const ExtRowSlots<D, NW> sl = ext_read_slots<D, NW>(sh, a, t + kExtAhead);
-  ext_slot_dma<D, NW>(sh, a, t + kExtSlotLead);
+  // the slot-id group that tile t + kExtAhead + G starts, if it starts one; it overwrites
+  // the group of tiles t + kExtAhead - G .. t + kExtAhead - 1, whose last ids were read in
+  // the iteration before
+  constexpr int G = kExtRingGroup<NW>;
+  if ((t + kExtAhead) % G == 0) ext_slot_dma<D, NW>(sh, a, (t + kExtAhead) / G + 1);
   ext_kv_dma<D, NW>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
   ext_qk<D, RB>(cur, kf, qf);
   ExtWeights<RB> w;
@@ -804,13 +813,14 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool first_pass) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
   const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
-  // prologue: slot ids of the first tiles, then their K/V
-  for (int x = 0; x < kExtSlotLead; ++x) ext_slot_dma<D, NW>(sh, a, x);
+  // prologue: the first two slot-id groups (the loop loads group k + 1 in the iteration
+  // that reads the first ids of group k), then the K/V of the first tiles
+  ext_slot_dma<D, NW>(sh, a, 0);
+  ext_slot_dma<D, NW>(sh, a, 1);
   wait_vmcnt_barrier<0>();
   for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
   // tile 0: its scores only
   ext_wait<D, NW>(0);
-  ext_slot_dma<D, NW>(sh, a, kExtSlotLead);
   f32x16 sprev[RB];
   KFrags<D> kf;
   VFrags<D> vf;
