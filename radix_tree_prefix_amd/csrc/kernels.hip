@@ -708,31 +708,29 @@ __device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStrea
   }
 }
 
-// Wait until tile t has landed for the whole workgroup (this wave's loads, then a
-// barrier).  Every iteration issues the tile kExtAhead ahead (2*kInstPerWave loads; past
-// the last tile they reload its last row into a stage nobody reads) and, one iteration in
-// kExtRingGroup, a slot-id group; loads complete in issue order: after tile t's loads come
-// at least those of the kExtAhead - 1 iterations since, so kAfter may stay outstanding
-// (a slot-id load among them only makes the wait longer).  Tiles issued before the loop
-// wait for all.
+// Waits on the K/V loads, each this wave's vmcnt count and then a barrier for everyone's.
+// Tiles 0 .. kExtAhead-1 are issued in order by the prologue, tile kExtAhead by the tile-0
+// step and tile t + kExtAhead by iteration t, each as 2*kInstPerWave loads (past the last
+// tile they reload its last row into a stage nobody reads), and loads complete in issue
+// order.  So when tile x is awaited while tiles up to x + kExtAhead - 2 have been issued,
+// exactly kExtAfter loads came after it (slot-id loads among them only make the wait
+// longer), whatever x.
 template <int D, int NW>
-__device__ __forceinline__ void ext_wait(int t) {
-  constexpr int kAfter = (kExtAhead - 1) * 2 * StageLayout<D, kExtKB, NW>::kInstPerWave;
-  static_assert(kAfter < 64, "vmcnt is 6 bits");
-  if (t >= kExtAhead) wait_vmcnt_barrier<kAfter>();
-  else wait_vmcnt_barrier<0>();
+constexpr int kExtAfter = (kExtAhead - 2) * 2 * StageLayout<D, kExtKB, NW>::kInstPerWave;
+
+// The tile-0 step needs tiles 0 and 1 (it reads tile 1's K ahead); tiles 2 .. kExtAhead-1
+// came after them.
+template <int D, int NW>
+__device__ __forceinline__ void ext_wait_first() {
+  static_assert(kExtAfter<D, NW> < 64, "vmcnt is 6 bits");
+  wait_vmcnt_barrier<kExtAfter<D, NW>>();
 }
 
-// Iteration t of the loop waits for tile t + 1 (its K is read ahead, at the end of
-// iteration t).  Tile t + 1 was issued by iteration t + 1 - kExtAhead (iteration 0 being
-// the tile-0 step), and kExtAhead - 2 iterations' loads came after it.  Everything issued
-// in iteration t + 1 - kExtAhead or earlier has then landed; that covers slot-id group k,
-// issued in iteration kG - kExtAhead - G and first read in iteration kG - kExtAhead.
+// Iteration t (t >= 1) needs tile t + 1 (its K is read ahead, at the end of the iteration);
+// tiles up to t + kExtAhead - 1 have been issued.
 template <int D, int NW>
-__device__ __forceinline__ void ext_wait_next(int t) {
-  constexpr int kAfter = (kExtAhead - 2) * 2 * StageLayout<D, kExtKB, NW>::kInstPerWave;
-  if (t + 1 >= kExtAhead) wait_vmcnt_barrier<kAfter>();
-  else wait_vmcnt_barrier<0>();
+__device__ __forceinline__ void ext_wait_next() {
+  wait_vmcnt_barrier<kExtAfter<D, NW>>();
 }
 
 // -inf in the scores of tile t past this lane's last visible key or the tile's last key (and,
@@ -772,7 +770,7 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
                                          const f32x16 (&prev)[RB], f32x16 (&cur)[RB], KFrags<D>& kf, VFrags<D>& vf,
                                          int t) {
-  ext_wait_next<D, NW>(t);
+  ext_wait_next<D, NW>();
   const ExtRowSlots<D, NW> sl = ext_read_slots<D, NW>(sh, a, t + kExtAhead);
   // the slot-id group that tile t + kExtAhead + G starts, if it starts one; it overwrites
   // the group of tiles t + kExtAhead - G .. t + kExtAhead - 1, whose last ids were read in
@@ -820,7 +818,7 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
   wait_vmcnt_barrier<0>();
   for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
   // tile 0: its scores only
-  ext_wait<D, NW>(0);
+  ext_wait_first<D, NW>();
   f32x16 sprev[RB];
   KFrags<D> kf;
   VFrags<D> vf;
@@ -830,8 +828,8 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
     ext_kv_dma<D, NW>(sh.st[kExtAhead % kExtNS], a, sl);
     f32x16 scur[RB];
     ext_qk<D, RB>(scur, kf, qf);
-    // every prologue tile has landed (the wait above counted to zero): tile 1's K and
-    // tile 0's V for the first iteration
+    // tiles 0 and 1 have landed (the wait above): tile 1's K and tile 0's V for the
+    // first iteration
     kf = ext_read_k<D>(sh.st[1 % kExtNS].k, off);
     vf = ext_read_v<D>(sh.st[0].v, off);
 #pragma unroll
