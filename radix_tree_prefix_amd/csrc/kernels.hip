@@ -806,16 +806,24 @@ __device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D, NW>&
 
 // One pass over keys [0, k1).  first_pass: each row's reference point is its maximum over
 // tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
+// ring_ready: this wave's first two slot-id groups have landed already.
 template <int D, int RB, bool TRACK, int NW>
 __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
-                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool first_pass) {
+                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool first_pass,
+                                         bool ring_ready) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
   const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
   // prologue: the first two slot-id groups (the loop loads group k + 1 in the iteration
   // that reads the first ids of group k), then the K/V of the first tiles
-  ext_slot_dma<D, NW>(sh, a, 0);
-  ext_slot_dma<D, NW>(sh, a, 1);
-  wait_vmcnt_barrier<0>();
+  if (!ring_ready) {
+    ext_slot_dma<D, NW>(sh, a, 0);
+    ext_slot_dma<D, NW>(sh, a, 1);
+    wait_vmcnt_barrier<0>();
+  } else {
+    // issued with the queries, which the caller has waited for already: this wave's own
+    // ring rows (no other wave reads them), whatever order the loads went out in
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
   // tile 0: its scores only
   ext_wait_first<D, NW>();
@@ -915,13 +923,20 @@ __device__ __forceinline__ void ext_rows(ExtShared<D, NW>& sh, ExtStream<D, NW>&
   bf16x8 qf[RB][D / 16];
   int64_t qrow_idx[RB];
   bool valid[RB];
+  // The first slot-id groups go out before the queries: the wait for the queries below
+  // (they are needed in AGPRs) then covers them too, one memory round trip for both.
+  ext_slot_dma<D, NW>(sh, a, 0);
+  ext_slot_dma<D, NW>(sh, a, 1);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = wave * 32 * RB + rb * 32 + (lane & 31);
     const int t = row / G, g = row % G;
     valid[rb] = t < ntok;
     qrow_idx[rb] = int64_t(qo + t0 + t) * Hq + kvh * G + g;
-    load_q<D>(qf[rb], q + qrow_idx[rb] * D, valid[rb], lane);
+    // A row past the tile's last token takes that token's query (its output is never
+    // stored and its scores only need to be finite), so every load is unconditional and
+    // they all go out together.
+    load_q<D>(qf[rb], q + (int64_t(qo + t0 + min(t, ntok - 1)) * Hq + kvh * G + g) * D, true, lane);
     a.lim[rb] = valid[rb] ? a.tree_base + t0 + t : -1;
     a.tm[rb] = (a.tree && valid[rb]) ? tree_mask[qo + t0 + t] : 0ull;
   }
@@ -938,13 +953,13 @@ __device__ __forceinline__ void ext_rows(ExtShared<D, NW>& sh, ExtStream<D, NW>&
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
   for (int pass = 0;; ++pass) {
-    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0);
+    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0, pass == 0);
     const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
     if (pass == 1 || !__syncthreads_or(overflow)) break;
     // Some weight overflowed: find each row's true maximum, then recompute the rows
     // with it as the reference (the outputs above are overwritten).
     ext_reset<D, RB>(es);
-    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true);
+    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true, false);
     float mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
