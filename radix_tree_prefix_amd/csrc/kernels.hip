@@ -880,37 +880,53 @@ __device__ __forceinline__ void ext_reset(ExtState<D, RB>& es) {
 
 // Write the valid rows' outputs O / l (bf16).  Returns true if any of them, or l, is not
 // finite: only an overflow of the weights makes that happen (x * 0 is 0 for finite x and
-// NaN for inf or NaN, so z is NaN exactly then).
+// NaN for inf or NaN, so z is NaN exactly then; four sums keep the chains short).
+// Lanes l and l ^ 32 hold the same row's d .. d+3 and d+4 .. d+7 of each 8-value group:
+// one v_permlane32_swap per register pair gives each lane 16 contiguous bytes of the
+// row (the lower lane the even group of a pair, the upper lane the odd one), so every
+// store writes 16 bytes per lane instead of 8 -- half the store instructions.
 template <int D, int RB>
 __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool (&valid)[RB], const int64_t (&qrow_idx)[RB],
                                           uint16_t* __restrict__ out, int lane) {
   const int hi = lane >> 5;
-  float z = 0.f;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if (!valid[rb]) continue;
     const float l = xhalf_sum(es.l[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    z = fmaf(l, 0.f, z);
+    z[0] = fmaf(l, 0.f, z[0]);
     uint16_t* orow = out + qrow_idx[rb] * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = mb * 32 + 8 * q4 + 4 * hi;
-        float v[4];
+      for (int pr = 0; pr < 2; ++pr) {
+        uint32_t w[2][2];          // [group of the pair][dword]: this lane's 4 values of d + 8 q4 + 4 hi
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = es.o[rb][mb][4 * q4 + e] * inv;
-          z = fmaf(v[e], 0.f, z);
+        for (int h = 0; h < 2; ++h) {
+          const int q4 = 2 * pr + h;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = es.o[rb][mb][4 * q4 + e] * inv;
+            z[e] = fmaf(v[e], 0.f, z[e]);
+          }
+          w[h][0] = pack_bf16(v[0], v[1]);
+          w[h][1] = pack_bf16(v[2], v[3]);
         }
-        uint2 u;
-        u.x = pack_bf16(v[0], v[1]);
-        u.y = pack_bf16(v[2], v[3]);
-        *reinterpret_cast<uint2*>(orow + d) = u;
+        // upper half of w[0] <-> lower half of w[1]: the lower lane then holds group 2pr
+        // (its own values, then its partner's), the upper lane group 2pr+1
+        uint4 u;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const auto r = __builtin_amdgcn_permlane32_swap(w[0][c], w[1][c], false, false);
+          (c == 0 ? u.x : u.y) = r[0];
+          (c == 0 ? u.z : u.w) = r[1];
+        }
+        *reinterpret_cast<uint4*>(orow + mb * 32 + 16 * pr + 8 * hi) = u;
       }
   }
-  return z != 0.f;                 // true for NaN
+  return (z[0] + z[1]) + (z[2] + z[3]) != 0.f;   // true for NaN
 }
 
 // The rows of one workgroup (RB 32-row blocks per wave, row = 32 (RB wave + block) + lane
