@@ -19,7 +19,8 @@
 // * decode: 4 waves of 32 rows (requests x heads), 64-key tiles, online softmax with a
 //   lazily moved reference point;
 // * extend: 4 waves of 64 rows (tokens x heads) in two row blocks, 32-key tiles, a
-//   software-pipelined loop and a per-row reference fixed from the first tile.
+//   software-pipelined loop and exponentials of the raw scaled scores (no reference point
+//   unless a row's range calls for one).
 // fp32 extend runs the same operand scheme on 32x32x2 fp32 MFMAs with operands loaded
 // straight into registers (workgroups of 32 query rows, 4 waves splitting the keys); fp32
 // decode runs on the VALU (one wave per query row).
@@ -455,14 +456,17 @@ __device__ __forceinline__ void stream_keys(WaveState<D>& ws, Stage<D, KB> (&sm)
 // the MFMA result registers to VGPRs (the copy is the pipeline's buffer swap); on the causal
 // diagonal or a ragged end it is then masked.
 //
-// Softmax reference.  Each row's reference point is the maximum of its scores in tile 0
-// and stays fixed for the pass, so the loop never rescales O and tracks no maximum.
-// Later scores may exceed it: the weights then exceed 1, which fp32 and bf16 carry with
-// the same relative precision up to their common overflow near 2^128.  Only an overflow
-// can spoil the result, and it leaves an inf or a NaN in O or l; the output check catches
-// that.  Then the workgroup finds each row's true maximum in a pass that tracks it and
-// recomputes its rows with that maximum as the reference (every weight <= 1).  Softmax
-// does not depend on the reference point.
+// Softmax reference.  Softmax does not depend on the reference point subtracted from the
+// scores before the exponential, and fp32 and bf16 carry a weight with the same relative
+// precision anywhere between their common underflow near 2^-126 and overflow near 2^128.
+// The first pass therefore subtracts nothing: a weight is exp2(S c) (one multiply before
+// the exponential instead of a three-operand fma), the loop never rescales O and tracks
+// no maximum.  Two things can spoil that: an overflow, which leaves an inf or a NaN in O
+// or l, and a row whose weights are all tiny, whose small products with small values
+// would fall below fp32's normal range; the output check catches both (l below 2^-40
+// stands for the second: the largest weight is then below 2^-40 too).  The workgroup then
+// finds each row's true maximum in a pass that tracks it and recomputes its rows with that
+// maximum as the reference (every weight <= 1, the largest one 1).
 constexpr int kExtKB = 32;           // keys per tile
 constexpr int kExtNS = 8;            // LDS stages (16 KiB each at d128)
 constexpr int kExtRows = 256;        // query rows per workgroup of the causal kernel: 4 waves x 64
@@ -479,7 +483,7 @@ static_assert(kExtRingGroup<4> > kExtAhead - 1 && kExtRingGroup<8> > kExtAhead -
 template <int D, int RB>
 struct ExtState {
   f32x16 o[RB][D / 32];         // O^T per row block (layout as WaveState)
-  float mc[RB];                 // reference point times c, per row block (fixed per pass)
+  float mc[RB];                 // reference point times c, per row block (recompute pass)
   float mx[RB];                 // this lane's running maximum of raw scores (tracking pass)
   float l[RB];                  // this lane's halves of the running sums
 };
@@ -555,9 +559,10 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return m;
 }
 
-// Weights P = bf16(exp2(S*c - m*c)) of both row blocks and their row sums (of the bf16
-// weights, as the second MFMA sees them); TRACK: also the running maxima of the scores.
-template <int D, int RB, bool TRACK>
+// Weights P = bf16(exp2(S*c)) of both row blocks (REF: bf16(exp2(S*c - m*c)) with the
+// reference m) and their row sums (of the bf16 weights, as the second MFMA sees them);
+// TRACK: also the running maxima of the scores.
+template <int D, int RB, bool TRACK, bool REF>
 __device__ __forceinline__ void ext_weights(ExtWeights<RB>& w, ExtState<D, RB>& es, const f32x16 (&sc)[RB], float c) {
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -568,7 +573,8 @@ __device__ __forceinline__ void ext_weights(ExtWeights<RB>& w, ExtState<D, RB>& 
     for (int kstep = 0; kstep < kExtKB / 16; ++kstep) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * kstep + i], c, -es.mc[rb]));
+      for (int i = 0; i < 8; ++i)
+        e[i] = __builtin_amdgcn_exp2f(REF ? fmaf(sc[rb][8 * kstep + i], c, -es.mc[rb]) : sc[rb][8 * kstep + i] * c);
       uint4& p = w.p[rb][kstep];
       p.x = pack_bf16(e[0], e[1]);
       p.y = pack_bf16(e[2], e[3]);
@@ -765,7 +771,7 @@ __device__ __forceinline__ void ext_mask(f32x16 (&sc)[RB], const ExtStream<D, NW
 // matrix cores while the VALU turns S(t-1) into weights, then O += V(t-1)^T P(t-1).  The
 // next K and V are read at the end, after the MFMAs are issued, so their LDS latency
 // overlaps the matrix work instead of delaying the next iteration's first MFMA.
-template <int D, int RB, bool MASK, bool TRACK, int NW>
+template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW>
 __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
                                          const f32x16 (&prev)[RB], f32x16 (&cur)[RB], KFrags<D>& kf, VFrags<D>& vf,
@@ -780,7 +786,7 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
   ext_kv_dma<D, NW>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
   ext_qk<D, RB>(cur, kf, qf);
   ExtWeights<RB> w;
-  ext_weights<D, RB, TRACK>(w, es, prev, a.c);
+  ext_weights<D, RB, TRACK, REF>(w, es, prev, a.c);
   ext_pv<D, RB>(es, vf, w);
   kf = ext_read_k<D>(sh.st[(t + 1) % kExtNS].k, off);
   vf = ext_read_v<D>(sh.st[t % kExtNS].v, off);
@@ -792,25 +798,24 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
 // S(t_end - 1) on exit.  (Unrolling by two so that two score buffers trade roles saves no
 // instruction: the scores come out of the MFMAs in accumulation registers and are moved to
 // VGPRs for the vector unit either way.)
-template <int D, int RB, bool MASK, bool TRACK, int NW>
+template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW>
 __device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
                                           f32x16 (&sprev)[RB], KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
   for (int t = t_begin; t < t_end; ++t) {
     f32x16 scur[RB];
-    ext_iter<D, RB, MASK, TRACK, NW>(es, sh, off, qf, a, sprev, scur, kf, vf, t);
+    ext_iter<D, RB, MASK, TRACK, REF, NW>(es, sh, off, qf, a, sprev, scur, kf, vf, t);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sprev[rb] = scur[rb];
   }
 }
 
-// One pass over keys [0, k1).  first_pass: each row's reference point is its maximum over
-// tile 0; otherwise es.mc holds it.  TRACK: es.mx gathers each lane's maximum score.
+// One pass over keys [0, k1).  REF: es.mc holds each row's reference point; otherwise the
+// weights are taken against none.  TRACK: es.mx gathers each lane's maximum score.
 // ring_ready: this wave's first two slot-id groups have landed already.
-template <int D, int RB, bool TRACK, int NW>
+template <int D, int RB, bool TRACK, bool REF, int NW>
 __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
-                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool first_pass,
-                                         bool ring_ready) {
+                                         const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool ring_ready) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
   const int t_mask = min(a.mask_from / kExtKB, a.ntiles);
   // prologue: the first two slot-id groups (the loop loads group k + 1 in the iteration
@@ -844,20 +849,12 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
     for (int rb = 0; rb < RB; ++rb) sprev[rb] = scur[rb];
     if (t_mask == 0) ext_mask<D, RB, NW>(sprev, a, 0);
   }
-  if (first_pass) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float m = max16(sprev[rb]);
-      m = fmaxf(m, __shfl_xor(m, 32));
-      es.mc[rb] = (m == -INFINITY ? 0.f : m) * a.c;
-    }
-  }
   const int t_split = max(1, t_mask);
-  ext_iters<D, RB, false, TRACK, NW>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
-  ext_iters<D, RB, true, TRACK, NW>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
+  ext_iters<D, RB, false, TRACK, REF, NW>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
+  ext_iters<D, RB, true, TRACK, REF, NW>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
   // the last tile's weights and P.V (vf holds its V)
   ExtWeights<RB> w;
-  ext_weights<D, RB, TRACK>(w, es, sprev, a.c);
+  ext_weights<D, RB, TRACK, REF>(w, es, sprev, a.c);
   ext_pv<D, RB>(es, vf, w);
   // the loads past the last tile have landed, and every wave is done with the stages and
   // the ring, before a later pass refills them or the workgroup ends
@@ -879,8 +876,9 @@ __device__ __forceinline__ void ext_reset(ExtState<D, RB>& es) {
 }
 
 // Write the valid rows' outputs O / l (bf16).  Returns true if any of them, or l, is not
-// finite: only an overflow of the weights makes that happen (x * 0 is 0 for finite x and
-// NaN for inf or NaN, so z is NaN exactly then; four sums keep the chains short).
+// finite -- only an overflow of the weights makes that happen (x * 0 is 0 for finite x and
+// NaN for inf or NaN, so z is NaN exactly then; four sums keep the chains short) -- or if
+// some valid row's l is below 2^-40 (weights taken against no reference, all tiny).
 // Lanes l and l ^ 32 hold the same row's d .. d+3 and d+4 .. d+7 of each 8-value group:
 // one v_permlane32_swap per register pair gives each lane 16 contiguous bytes of the
 // row (the lower lane the even group of a pair, the upper lane the odd one), so every
@@ -890,12 +888,14 @@ __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool 
                                           uint16_t* __restrict__ out, int lane) {
   const int hi = lane >> 5;
   float z[4] = {0.f, 0.f, 0.f, 0.f};
+  bool tiny = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if (!valid[rb]) continue;
     const float l = xhalf_sum(es.l[rb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     z[0] = fmaf(l, 0.f, z[0]);
+    tiny |= l < 0x1p-40f;
     uint16_t* orow = out + qrow_idx[rb] * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
@@ -926,7 +926,7 @@ __device__ __forceinline__ bool ext_store(const ExtState<D, RB>& es, const bool 
         *reinterpret_cast<uint4*>(orow + mb * 32 + 16 * pr + 8 * hi) = u;
       }
   }
-  return (z[0] + z[1]) + (z[2] + z[3]) != 0.f;   // true for NaN
+  return tiny || (z[0] + z[1]) + (z[2] + z[3]) != 0.f;   // true for NaN
 }
 
 // The rows of one workgroup (RB 32-row blocks per wave, row = 32 (RB wave + block) + lane
@@ -968,20 +968,20 @@ __device__ __forceinline__ void ext_rows(ExtShared<D, NW>& sh, ExtStream<D, NW>&
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
-  for (int pass = 0;; ++pass) {
-    ext_pass<D, RB, false, NW>(es, sh, off, qf, a, pass == 0, pass == 0);
-    const bool overflow = ext_store<D, RB>(es, valid, qrow_idx, out, lane);
-    if (pass == 1 || !__syncthreads_or(overflow)) break;
-    // Some weight overflowed: find each row's true maximum, then recompute the rows
-    // with it as the reference (the outputs above are overwritten).
+  ext_pass<D, RB, false, false, NW>(es, sh, off, qf, a, true);
+  if (__syncthreads_or(ext_store<D, RB>(es, valid, qrow_idx, out, lane))) {
+    // A weight overflowed or some row's weights are all tiny: find each row's true maximum,
+    // then recompute the rows with it as the reference (the outputs above are overwritten).
     ext_reset<D, RB>(es);
-    ext_pass<D, RB, true, NW>(es, sh, off, qf, a, true, false);
+    ext_pass<D, RB, true, false, NW>(es, sh, off, qf, a, false);
     float mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
     ext_reset<D, RB>(es);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) es.mc[rb] = (mx[rb] == -INFINITY ? 0.f : mx[rb]) * a.c;
+    ext_pass<D, RB, false, true, NW>(es, sh, off, qf, a, false);
+    ext_store<D, RB>(es, valid, qrow_idx, out, lane);
   }
 }
 

@@ -188,6 +188,13 @@ def _planted_case(torch, rs, sm, lens, seed, dtname="bf16"):
         off += n
         p = lens[b][0]
         kp[table[b, p - 7]] = q[qo[b], 0:Hq:Hq // Hkv]     # key p-7 of KV head h = query 0's head h*G
+    return _extend_vs_oracle(torch, rs, q, kp, vp, table, lens, sm, dtname)
+
+
+def _extend_vs_oracle(torch, rs, q, kp, vp, table, lens, sm, dtname):
+    """Extend over the given pools and index table, every row against oracle.attend."""
+    ext = np.array([e for _, e in lens], np.int32)
+    qo = np.concatenate([[0], np.cumsum(ext)]).astype(np.int32)
     dt = torch.bfloat16 if dtname == "bf16" else torch.float32
     out = rs.extend_attention(_to_dev(torch, q, dt), _to_dev(torch, kp, dt),
                               _to_dev(torch, vp, dt), _to_dev(torch, table, torch.int32),
@@ -205,9 +212,10 @@ def _planted_case(torch, rs, sm, lens, seed, dtname="bf16"):
 
 @pytest.mark.parametrize("sm", [0.35, 0.6, 1.0])
 def test_extend_late_dominant_key(torch_rs, sm):
-    """A late score far above the first tile's maximum (about 0.35, 0.6 or 1.0 x 185
-    log2-units): weights up to ~2^110 stay finite and exact relative to each other; at
-    sm=1 they overflow fp32, and the rows are recomputed with their true maximum."""
+    """A late score far above every other (about 0.35, 0.6 or 1.0 x 185 log2-units, and
+    far above the first tile's maximum): weights up to ~2^110 stay finite and exact
+    relative to each other; at sm=1 they overflow fp32, and the rows are recomputed with
+    their true maximum."""
     torch, rs = torch_rs
     lens = [(100, 50), (700, 37), (3000, 64)]
     _say(f"extend planted dominant key sm_scale={sm} lens={lens}")
@@ -224,6 +232,31 @@ def test_extend_f32_late_dominant_key(torch_rs, sm):
     _say(f"extend f32 planted dominant key sm_scale={sm} lens={lens}")
     err = _planted_case(torch, rs, sm, lens, seed=11, dtname="f32")
     assert err <= TOL["f32"], err
+
+
+@pytest.mark.parametrize("dtname", ["bf16", "f32"])
+def test_extend_all_scores_far_below_zero(torch_rs, dtname):
+    """Every score of every row sits about 260 log2-units below zero (queries near -16, keys
+    near +1 in every dimension), so weights taken against no reference all underflow to 0:
+    the rows must come out of a pass with their true maximum as the reference."""
+    torch, rs = torch_rs
+    Hq, Hkv, D = 8, 2, 128
+    lens = [(0, 70), (100, 50), (700, 37), (3000, 64)]
+    _say(f"extend {dtname} scores far below zero lens={lens}")
+    rng = np.random.default_rng(19)
+    L = [p + e for p, e in lens]
+    S = sum(L) + 5
+    kp = _bf16((1.0 + 0.5 * rng.standard_normal((S, Hkv, D))).astype(np.float32))
+    vp = _bf16(rng.standard_normal((S, Hkv, D)).astype(np.float32))
+    q = _bf16((-16.0 + rng.standard_normal((sum(e for _, e in lens), Hq, D))).astype(np.float32))
+    perm = rng.permutation(S).astype(np.int32)
+    table = np.full((len(lens), max(L)), -1, np.int32)
+    off = 0
+    for b, n in enumerate(L):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    err = _extend_vs_oracle(torch, rs, q, kp, vp, table, lens, 1 / np.sqrt(D), dtname)
+    assert err <= TOL[dtname], err
 
 
 def test_extend_prefix_zero_is_textbook_causal(torch_rs):
