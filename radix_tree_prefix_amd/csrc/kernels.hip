@@ -142,7 +142,12 @@ __device__ __forceinline__ TileSlots<D, KB> wave_slots(const int32_t* __restrict
   return t;
 }
 
-// Issue the global->LDS loads of one tile (this wave's KB/4 rows of K and of V).
+// Cache-policy operand of the load builtins: non-temporal.  Decode reads every KV byte once
+// per launch (a shared segment once for all the requests that share it).
+constexpr int kCpolNT = 2;
+
+// Issue the global->LDS loads of one tile (this wave's KB/4 rows of K and of V), with the
+// non-temporal policy.
 // co[g] = this lane's byte offset within its row for instruction g (its swizzled chunk).
 template <int D, int KB>
 __device__ __forceinline__ void issue_tile(Stage<D, KB>& dst, const char* kp, const char* vp, uint32_t row_bytes,
@@ -153,8 +158,8 @@ __device__ __forceinline__ void issue_tile(Stage<D, KB>& dst, const char* kp, co
   for (int g = 0; g < L::kInstPerWave; ++g) {
     const uint64_t off = uint64_t(uint32_t(ts.s[g])) * row_bytes + co[g];
     const int r0 = wave_u * L::kRowsPerWave + g * L::kRowsPerInst;
-    __builtin_amdgcn_global_load_lds(kp + off, (lds_ptr)(dst.k + r0 * L::kRow), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + off, (lds_ptr)(dst.v + r0 * L::kRow), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kp + off, (lds_ptr)(dst.k + r0 * L::kRow), 16, 0, kCpolNT);
+    __builtin_amdgcn_global_load_lds(vp + off, (lds_ptr)(dst.v + r0 * L::kRow), 16, 0, kCpolNT);
   }
 }
 
@@ -666,8 +671,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(uintptr_t((__attribute__((address_space(3))) const void*)(p)));
 }
 
+// NT: with the non-temporal cache policy, for bytes the launch reads only once.
+template <bool NT>
 __device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {   // lane l -> lds + 16*l
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+  if (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
 }
 
 __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {    // lane l -> lds + 4*l
@@ -701,16 +711,16 @@ __device__ __forceinline__ ExtRowSlots<D, NW> ext_read_slots(const ExtShared<D, 
   return r;
 }
 
-// Global -> LDS loads of this wave's K and V rows of one tile.
-template <int D, int NW>
+// Global -> LDS loads of this wave's K and V rows of one tile (NT: non-temporal).
+template <int D, int NW, bool NT>
 __device__ __forceinline__ void ext_kv_dma(Stage<D, kExtKB>& dst, const ExtStream<D, NW>& a, const ExtRowSlots<D, NW>& sl) {
   using L = StageLayout<D, kExtKB, NW>;
 #pragma unroll
   for (int g = 0; g < L::kInstPerWave; ++g) {
     const uint64_t off = uint64_t(uint32_t(sl.s[g])) * a.row_bytes + a.co[g];
     const int r0 = a.wave_u * L::kRowsPerWave + g * L::kRowsPerInst;
-    dma_b128(a.kc + off, lds_addr(dst.k + r0 * L::kRow));
-    dma_b128(a.vc + off, lds_addr(dst.v + r0 * L::kRow));
+    dma_b128<NT>(a.kc + off, lds_addr(dst.k + r0 * L::kRow));
+    dma_b128<NT>(a.vc + off, lds_addr(dst.v + r0 * L::kRow));
   }
 }
 
@@ -766,12 +776,12 @@ __device__ __forceinline__ void ext_mask(f32x16 (&sc)[RB], const ExtStream<D, NW
   }
 }
 
-// Iteration t (t >= 1): on entry prev holds S(t-1) (relative to the reference, masked), kf
+// Iteration t (t >= 1): on entry prev holds S(t-1) (masked), kf
 // K(t) and vf V(t-1); on exit cur holds S(t), kf K(t+1) and vf V(t).  S(t) runs on the
 // matrix cores while the VALU turns S(t-1) into weights, then O += V(t-1)^T P(t-1).  The
 // next K and V are read at the end, after the MFMAs are issued, so their LDS latency
 // overlaps the matrix work instead of delaying the next iteration's first MFMA.
-template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW>
+template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW, bool NT>
 __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
                                          const f32x16 (&prev)[RB], f32x16 (&cur)[RB], KFrags<D>& kf, VFrags<D>& vf,
@@ -783,7 +793,7 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
   // the iteration before
   constexpr int G = kExtRingGroup<NW>;
   if ((t + kExtAhead) % G == 0) ext_slot_dma<D, NW>(sh, a, (t + kExtAhead) / G + 1);
-  ext_kv_dma<D, NW>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
+  ext_kv_dma<D, NW, NT>(sh.st[(t + kExtAhead) % kExtNS], a, sl);
   ext_qk<D, RB>(cur, kf, qf);
   ExtWeights<RB> w;
   ext_weights<D, RB, TRACK, REF>(w, es, prev, a.c);
@@ -798,13 +808,13 @@ __device__ __forceinline__ void ext_iter(ExtState<D, RB>& es, ExtShared<D, NW>& 
 // S(t_end - 1) on exit.  (Unrolling by two so that two score buffers trade roles saves no
 // instruction: the scores come out of the MFMAs in accumulation registers and are moved to
 // VGPRs for the vector unit either way.)
-template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW>
+template <int D, int RB, bool MASK, bool TRACK, bool REF, int NW, bool NT>
 __device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a,
                                           f32x16 (&sprev)[RB], KFrags<D>& kf, VFrags<D>& vf, int t_begin, int t_end) {
   for (int t = t_begin; t < t_end; ++t) {
     f32x16 scur[RB];
-    ext_iter<D, RB, MASK, TRACK, REF, NW>(es, sh, off, qf, a, sprev, scur, kf, vf, t);
+    ext_iter<D, RB, MASK, TRACK, REF, NW, NT>(es, sh, off, qf, a, sprev, scur, kf, vf, t);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sprev[rb] = scur[rb];
   }
@@ -812,8 +822,9 @@ __device__ __forceinline__ void ext_iters(ExtState<D, RB>& es, ExtShared<D, NW>&
 
 // One pass over keys [0, k1).  REF: es.mc holds each row's reference point; otherwise the
 // weights are taken against none.  TRACK: es.mx gathers each lane's maximum score.
-// ring_ready: this wave's first two slot-id groups have landed already.
-template <int D, int RB, bool TRACK, bool REF, int NW>
+// ring_ready: this wave's first two slot-id groups have landed already.  NT: K/V loads with
+// the non-temporal cache policy.
+template <int D, int RB, bool TRACK, bool REF, int NW, bool NT>
 __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& sh, const ExtOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16], const ExtStream<D, NW>& a, bool ring_ready) {
   // tiles from t_mask on hold keys at or past mask_from: the causal diagonal, the ragged end
@@ -829,7 +840,7 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
     // ring rows (no other wave reads them), whatever order the loads went out in
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
+  for (int x = 0; x < kExtAhead; ++x) ext_kv_dma<D, NW, NT>(sh.st[x], a, ext_read_slots<D, NW>(sh, a, x));
   // tile 0: its scores only
   ext_wait_first<D, NW>();
   f32x16 sprev[RB];
@@ -838,7 +849,7 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
   {
     const ExtRowSlots<D, NW> sl = ext_read_slots<D, NW>(sh, a, kExtAhead);
     kf = ext_read_k<D>(sh.st[0].k, off);
-    ext_kv_dma<D, NW>(sh.st[kExtAhead % kExtNS], a, sl);
+    ext_kv_dma<D, NW, NT>(sh.st[kExtAhead % kExtNS], a, sl);
     f32x16 scur[RB];
     ext_qk<D, RB>(scur, kf, qf);
     // tiles 0 and 1 have landed (the wait above): tile 1's K and tile 0's V for the
@@ -850,8 +861,8 @@ __device__ __forceinline__ void ext_pass(ExtState<D, RB>& es, ExtShared<D, NW>& 
     if (t_mask == 0) ext_mask<D, RB, NW>(sprev, a, 0);
   }
   const int t_split = max(1, t_mask);
-  ext_iters<D, RB, false, TRACK, REF, NW>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
-  ext_iters<D, RB, true, TRACK, REF, NW>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
+  ext_iters<D, RB, false, TRACK, REF, NW, NT>(es, sh, off, qf, a, sprev, kf, vf, 1, t_split);
+  ext_iters<D, RB, true, TRACK, REF, NW, NT>(es, sh, off, qf, a, sprev, kf, vf, t_split, a.ntiles);
   // the last tile's weights and P.V (vf holds its V)
   ExtWeights<RB> w;
   ext_weights<D, RB, TRACK, REF>(w, es, sprev, a.c);
@@ -968,19 +979,23 @@ __device__ __forceinline__ void ext_rows(ExtShared<D, NW>& sh, ExtStream<D, NW>&
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) asm volatile("" : "+a"(es.o[rb][mb]));
   }
-  ext_pass<D, RB, false, false, NW>(es, sh, off, qf, a, true);
+  // The draft-tree verify reads each request's keys once per KV head (one workgroup holds
+  // all its verify tokens): those loads take the non-temporal policy.  A causal q-tile
+  // shares its request's prefix with the request's other q-tiles, which find it in the
+  // caches when they run together; its loads keep the default policy.
+  ext_pass<D, RB, false, false, NW, TREE>(es, sh, off, qf, a, true);
   if (__syncthreads_or(ext_store<D, RB>(es, valid, qrow_idx, out, lane))) {
     // A weight overflowed or some row's weights are all tiny: find each row's true maximum,
     // then recompute the rows with it as the reference (the outputs above are overwritten).
     ext_reset<D, RB>(es);
-    ext_pass<D, RB, true, false, NW>(es, sh, off, qf, a, false);
+    ext_pass<D, RB, true, false, NW, TREE>(es, sh, off, qf, a, false);
     float mx[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) mx[rb] = xhalf_max(es.mx[rb]);
     ext_reset<D, RB>(es);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) es.mc[rb] = (mx[rb] == -INFINITY ? 0.f : mx[rb]) * a.c;
-    ext_pass<D, RB, false, true, NW>(es, sh, off, qf, a, false);
+    ext_pass<D, RB, false, true, NW, TREE>(es, sh, off, qf, a, false);
     ext_store<D, RB>(es, valid, qrow_idx, out, lane);
   }
 }
