@@ -1268,8 +1268,9 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
 //                   floats of dims (D/32)(l%32) ...
 // A wave loads tile t + 4 (and the slot ids of tile t + 8) before it computes tile t.
 //
-// Softmax reference, as in the bf16 extend engine: a wave fixes each row's reference at
-// the row's maximum in the first tile the wave computes and never moves it, so the loop
+// Softmax reference: a wave fixes each row's reference at the row's maximum in the first
+// tile the wave computes and never moves it (the bf16 engine's first pass takes none;
+// here the reference costs no instruction, as below), so the loop
 // tracks no maximum and never rescales O (the VALU work of a tile is the exp2 and the row
 // sums; measured on gfx950, fp32 MFMAs leave little VALU issue alongside them).  The
 // reference enters the scores through the accumulator: the QK chain starts from -ref,
