@@ -4,7 +4,8 @@ The check must be able to fail where it matters: on the longest contexts of the 
 batch (about 32k keys), whose outputs are small.  Here the oracle's own input is damaged
 on purpose (one aligned 32-key tile of the context removed) and the check must reject the
 result; a correct bf16 computation of the same request (fp32 scores, weights rounded to
-bf16 against the first tile's maximum, fp32 sums, output rounded to bf16) must pass it.
+bf16 against the first tile's maximum or against no reference point, fp32 sums, output
+rounded to bf16) must pass it.
 Both a decode request (its one query) and an extend request (query rows at the end of its
 512-token chunk) are tried.
 """
@@ -20,8 +21,9 @@ def _bf(x):
     return synth._round_bf16(np.asarray(x, np.float32)).astype(np.float64)
 
 
-def _bf16_attention(q, K, V, pos, sm):
-    """What a correct bf16 kernel computes, on the CPU."""
+def _bf16_attention(q, K, V, pos, sm, ref):
+    """What a correct bf16 kernel computes, on the CPU: weights exp(s - m) rounded to bf16,
+    with m each row's maximum over the first 32 keys (ref="tile0") or m = 0 (ref="none")."""
     n, Hq, D = q.shape
     G = Hq // K.shape[1]
     out = np.empty((n, Hq, D))
@@ -29,7 +31,7 @@ def _bf16_attention(q, K, V, pos, sm):
     for h in range(Hq):
         s = sm * (q[:, h, :].astype(np.float64) @ K[:, h // G, :].T.astype(np.float64))
         s[hidden] = -np.inf
-        m = s[:, :32].max(1, keepdims=True)
+        m = s[:, :32].max(1, keepdims=True) if ref == "tile0" else 0.0
         p = _bf(np.exp(s - m))
         out[:, h, :] = _bf((p @ V[:, h // G, :]) / p.sum(1, keepdims=True))
     return out
@@ -42,7 +44,8 @@ def mixed():
 
 
 @pytest.mark.parametrize("kind", ["decode", "extend"])
-def test_check_rejects_one_dropped_tile_at_32k(mixed, kind):
+@pytest.mark.parametrize("weight_ref", ["tile0", "none"])
+def test_check_rejects_one_dropped_tile_at_32k(mixed, kind, weight_ref):
     wl, vals = mixed
     reqs = wl.decode_requests() if kind == "decode" else wl.extend_requests()
     r = max(reqs, key=lambda r: r.seq_len)
@@ -55,7 +58,7 @@ def test_check_rejects_one_dropped_tile_at_32k(mixed, kind):
     q = vals.q_rows(r.tokens, 0, r.seq_len)[rows]
     ref, _ = oracle.attend(q, k, v, rows, wl.sm_scale)
     # a correct bf16 result passes
-    good = _bf16_attention(q, k, v, rows, wl.sm_scale)
+    good = _bf16_attention(q, k, v, rows, wl.sm_scale, weight_ref)
     assert bf16_request_ok(good, ref), bf16_request_errors(good, ref)
     # one 32-key tile in the middle of the context left out: rejected, although its
     # max-abs error alone is well inside the stated 2e-2
