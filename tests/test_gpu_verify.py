@@ -40,11 +40,13 @@ def _parents(rng, n, chain=False):
     return np.array([-1] + [int(rng.integers(0, i)) for i in range(1, n)], np.int32)
 
 
-def _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed, chain=False):
+def _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed, chain=False, far_below=False):
+    """far_below: keys near +1 and queries near -16 in every dimension, so that every score
+    sits far below zero (hundreds of log2-units)."""
     rng = np.random.default_rng(seed)
     B = len(prefixes)
     S = int(sum(prefixes)) + B * n + 17
-    kp = _bf16(rng.standard_normal((S, Hkv, D)))
+    kp = _bf16(rng.standard_normal((S, Hkv, D)) * (0.5 if far_below else 1.0) + (1.0 if far_below else 0.0))
     vp = _bf16(rng.standard_normal((S, Hkv, D)))
     perm = rng.permutation(S).astype(np.int32)
     ld = max(prefixes) + n
@@ -55,7 +57,7 @@ def _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed, chain=False):
         off += p + n
     parents = np.stack([_parents(rng, n, chain) for _ in range(B)])
     mask, pos, _nt, _ns = rs.draft_tree_build(parents, np.array(prefixes, np.int32))
-    q = _bf16(rng.standard_normal((B * n, Hq, D)))
+    q = _bf16(rng.standard_normal((B * n, Hq, D)) - (16.0 if far_below else 0.0))
     sm = 1 / np.sqrt(D)
     out = rs.tree_verify_attention(_dev(torch, q, torch.bfloat16), _dev(torch, kp, torch.bfloat16),
                                    _dev(torch, vp, torch.bfloat16), _dev(torch, table, torch.int32),
@@ -72,13 +74,30 @@ def test_tree_verify_against_oracle(torch_rs, Hq, Hkv, D, n):
     prefixes = [0, 37, 1000]
     _say(f"tree verify Hq={Hq} Hkv={Hkv} D={D} n={n} prefixes={prefixes}")
     c = _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed=n + D)
-    worst = 0.0
-    for b, p in enumerate(prefixes):
+    worst = _worst_vs_oracle(c)
+    assert worst <= TOL_BF16, worst
+
+
+def _worst_vs_oracle(c):
+    n, worst = c["n"], 0.0
+    for b, p in enumerate(c["prefixes"]):
         row = c["table"][b]
         ref = oracle.speculative.verify_attention(c["q"][b * n:(b + 1) * n], c["kp"][row[:p]], c["vp"][row[:p]],
                                                   c["kp"][row[p:p + n]], c["vp"][row[p:p + n]], c["parents"][b],
                                                   c["sm"])
         worst = max(worst, float(np.abs(c["got"][b * n:(b + 1) * n] - ref).max()))
+    return worst
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,n", [(64, 8, 128, 16), (8, 8, 64, 5)])
+def test_tree_verify_scores_far_below_zero(torch_rs, Hq, Hkv, D, n):
+    """Every score hundreds of log2-units below zero: weights taken against no reference
+    point all underflow, and the rows must come from the pass with their true maximum."""
+    torch, rs = torch_rs
+    prefixes = [0, 37, 1000]
+    _say(f"tree verify far below zero Hq={Hq} Hkv={Hkv} D={D} n={n}")
+    c = _verify_case(torch, rs, Hq, Hkv, D, prefixes, n, seed=3 * n + D, far_below=True)
+    worst = _worst_vs_oracle(c)
     assert worst <= TOL_BF16, worst
 
 
