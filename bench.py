@@ -309,7 +309,9 @@ def cpu_baseline(st, budget_s=20.0):
 
 EXTEND_KERNEL = "extend_bf16_kernel<128, false, 4, 2>"
 VERIFY_KERNEL = "extend_bf16_kernel<128, true, 4, 1>"
-DECODE_KERNEL = "decode_bf16_kernel<128>"
+# the decode kernel is instantiated per cache policy (<128, true> streams with the non-temporal
+# one); a workload runs one of them, and the pattern names whichever it is
+DECODE_KERNEL = "decode_bf16_kernel<128, *>"
 MERGE_KERNEL = "decode_merge_kernel<128>"
 F32_KERNEL = "extend_f32_kernel<64, 4>"
 
@@ -325,19 +327,31 @@ def code_hash(path):
     return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
 
 
+def kernel_record(kernels, pattern):
+    """(name, record) of the one kernel in `kernels` whose name matches `pattern` (an exact
+    name, or an fnmatch pattern such as DECODE_KERNEL), else (pattern, None)."""
+    import fnmatch
+    if pattern in kernels:
+        return pattern, kernels[pattern]
+    hits = [n for n in kernels if fnmatch.fnmatchcase(n, pattern)]
+    return (hits[0], kernels[hits[0]]) if len(hits) == 1 else (pattern, None)
+
+
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` ("5", "1", "2", "3", "4", "verify") from the
-    committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's reading), or None
-    when the kernel source has changed since they were taken or they do not cover the pair."""
+    """HBM bytes per launch of `kernel` (a name or pattern) on `workload` ("5", "1", "2", "3",
+    "4", "verify") from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a plain
+    copy's reading), or None when the kernel source has changed since they were taken or they
+    do not cover the pair."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    k = rec["workloads"].get(str(workload), {}).get("kernels", {}).get(kernel)
+    name, k = kernel_record(rec["workloads"].get(str(workload), {}).get("kernels", {}), kernel)
     if code_hash(os.path.join(here, rec["source"])) != rec["code_sha256"] or k is None:
         return None
-    return {"bytes": k["read_bytes"] + k["write_bytes"], "read": k["read_bytes"], "write": k["write_bytes"]}
+    return {"bytes": k["read_bytes"] + k["write_bytes"], "read": k["read_bytes"], "write": k["write_bytes"],
+            "kernel": name}
 
 
 # ---------------------------------------------------------------------------- main
@@ -435,6 +449,7 @@ def main():
         tr = measured_traffic(roof["kernel"], args.config)
         if tr is not None:
             roof["traffic"] = tr["bytes"]
+            roof["kernel"] = tr["kernel"]
     out = {
         "metric": "decode+extend attention tokens/s and achieved HBM GB/s (% peak), 1 MI355X",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
